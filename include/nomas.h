@@ -1,0 +1,199 @@
+/*
+ * nomas.h -- C ABI of libnomas.so: the segment-attention hot path of a
+ * segment-autoregressive video diffusion transformer, for AMD MI355X (gfx950).
+ *
+ * The path, as the pages describe the model:
+ *   - the DiT renders one video segment at a time and conditions it on a cache
+ *     of earlier latents' keys and values ("Hy-Nomas: Was Tencent mit seinem frei
+ *     formbaren interaktiven Weltmodell tatsaechlich macht", orcarouter.ai,
+ *     section "Die Schleife");
+ *   - 54 double-stream blocks, hidden 2048 = 16 heads x 128, 3D RoPE
+ *     ("Hy-Nomas auf einer RTX 4090", inferencekey.com, section
+ *     "Modell und Dateien");
+ *   - on one GPU the cache keeps a window of the last 18 latent frames, stored
+ *     INT8 and computed BF16 (same page, section "Das Single-GPU-Preset";
+ *     blog.authon.dev config excerpt: kv_cache_quantization: int8,
+ *     sliding_window.past_frames: 18);
+ *   - segment-wise causal joint attention (madebyagents.com model page
+ *     "Hy-Nomas", component "Segment-Autoregressive DiT").
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are HIP device pointers, (host) are host memory.
+ *     bf16 data is passed as uint16_t bit patterns.
+ *   - The caller owns all memory. The library never allocates, frees or
+ *     synchronises; every compute call enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *   - Every call returns a nomas_status. All arguments are checked on the host
+ *     before anything is enqueued: on an error nothing is enqueued, the cache
+ *     descriptor is unchanged, and nomas_last_error() describes the problem.
+ *     NOMAS_E_HIP reports a failed kernel launch (hipGetErrorString text).
+ *   - Inputs holding NaN or Inf give undefined results (not checked).
+ *   - Activations are token-major: element (row r, head h, dim d) of a tensor
+ *     with row stride `ld` (elements) is at base[r*ld + h*head_dim + d].
+ *     `ld` >= n_heads*head_dim and a multiple of 8; base pointers 16-byte
+ *     aligned. This lets Q, K and V be views into one fused QKV buffer.
+ *   - Supported: head_dim in {64, 128}; n_heads >= 1.
+ */
+#ifndef NOMAS_H
+#define NOMAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NOMAS_OK = 0,
+  NOMAS_E_INVALID = 1,      /* bad argument (null, size, alignment, layout)   */
+  NOMAS_E_UNSUPPORTED = 2,  /* valid but not implemented (e.g. head_dim 96)   */
+  NOMAS_E_WORKSPACE = 3,    /* workspace missing or smaller than required     */
+  NOMAS_E_HIP = 4           /* a HIP runtime call or kernel launch failed     */
+} nomas_status;
+
+typedef enum { NOMAS_KV_BF16 = 0, NOMAS_KV_INT8 = 1 } nomas_kv_dtype;
+
+/*
+ * Ring-buffer KV cache of one layer: a window of `capacity_frames` latent
+ * frames of `tokens_per_frame` video tokens each. Caller-owned plain data;
+ * fill it with nomas_kvcache_init. Only nomas_kvcache_append changes it
+ * (frames_written).
+ *
+ * Frame f of the session (f = 0, 1, ... in append order) is stored in slot
+ * f mod capacity_frames while it is retained; the retained frames are the last
+ * min(frames_written, capacity_frames) appended, so they always fill slots
+ * [0, valid_frames) and token rows [0, valid_frames*tokens_per_frame).
+ *
+ * Device layouts (token_pitch = nomas_kvcache_token_pitch(...), a multiple of
+ * 128 >= capacity_frames*tokens_per_frame; slot token s = slot*tpf + i):
+ *   k        [n_heads][token_pitch][head_dim]   bf16 or int8, row-major
+ *   v        [n_heads][head_dim][token_pitch]   bf16 or int8, TRANSPOSED: the
+ *            tokens of one (head, dim) are contiguous, which is the operand
+ *            order the attention kernel's value contraction reads
+ *   k_scale, v_scale  [n_heads][token_pitch]   float32, INT8 only (else NULL)
+ * INT8 entries are x ~= code * scale with one scale per (token, head) vector.
+ */
+typedef struct nomas_kvcache {
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t tokens_per_frame;
+  int32_t capacity_frames;
+  int32_t kv_dtype;          /* nomas_kv_dtype */
+  int32_t token_pitch;
+  void* k;                   /* (device) */
+  void* v;                   /* (device) */
+  float* k_scale;            /* (device) INT8 only */
+  float* v_scale;            /* (device) INT8 only */
+  int64_t frames_written;    /* frames appended since init */
+} nomas_kvcache;
+
+/* Library version, (major << 16) | minor. */
+int32_t nomas_version(void);
+
+/* Text of the last error on the calling thread ("" if none). Valid until the
+ * next call into the library on that thread. */
+const char* nomas_last_error(void);
+
+/* Tokens reserved per head in the cache buffers: round_up(capacity*tpf, 128).
+ * Returns -1 on invalid sizes. */
+int64_t nomas_kvcache_token_pitch(int32_t tokens_per_frame, int32_t capacity_frames);
+
+/* Bytes of one cache buffer: which = 0 -> k, 1 -> v, 2 -> one scale array
+ * (0 for NOMAS_KV_BF16). Returns 0 on invalid arguments. */
+size_t nomas_kvcache_bytes(int32_t n_heads, int32_t head_dim, int32_t tokens_per_frame,
+                           int32_t capacity_frames, int32_t kv_dtype, int32_t which);
+
+/* Fill `*c` (host) for caller-allocated device buffers of the sizes above, with
+ * frames_written = 0. Scales must be NULL for BF16 and non-NULL for INT8.
+ * Buffer contents need no initialisation. */
+int32_t nomas_kvcache_init(nomas_kvcache* c, int32_t n_heads, int32_t head_dim,
+                           int32_t tokens_per_frame, int32_t capacity_frames, int32_t kv_dtype,
+                           void* k, void* v, float* k_scale, float* v_scale);
+
+/* Number of retained frames, min(frames_written, capacity_frames); -1 if c is NULL. */
+int64_t nomas_kvcache_valid_frames(const nomas_kvcache* c);
+
+/*
+ * 3D rotary position embedding, in place, of the n_frames*grid_h*grid_w video
+ * rows of q (and of k when k != NULL). Text rows are not passed and not rotated.
+ * Row i (ordered frame, row, col) sits at t = t0 + i/(grid_h*grid_w),
+ * h = (i/grid_w) % grid_h, w = i % grid_w. Head-dim bands [0,d_t), [d_t,d_t+d_h),
+ * [d_t+d_h,head_dim) are rotated by t, h, w: channels (o+2j, o+2j+1) of a band
+ * of width d turn by pos*theta^(-2j/d) (negated when inverse != 0).
+ * Pages: "3D RoPE" in the model card's architecture list ("Hy-Nomas auf einer
+ * RTX 4090", section "Modell und Dateien"); band split, pair order and theta are
+ * this library's reading (arguments).
+ * Arithmetic: per-pair frequency theta^(-2j/d) evaluated in double precision on
+ * the host and rounded to float32; angle, sine/cosine and rotation in float32;
+ * result rounded to bf16 (nearest even).
+ * q, k: (device) [rows][ld] bf16. d_t + d_h + d_w == head_dim, each even.
+ * t0 >= 0, n_frames >= 1, grid_h, grid_w >= 1, theta > 0.
+ */
+int32_t nomas_rope3d(uint16_t* q, uint16_t* k, int64_t ld, int32_t n_heads, int32_t head_dim,
+                     int32_t t0, int32_t n_frames, int32_t grid_h, int32_t grid_w,
+                     int32_t d_t, int32_t d_h, int32_t d_w, float theta, int32_t inverse,
+                     void* stream);
+
+/*
+ * Append n_frames latent frames (n_frames*tokens_per_frame video rows of K and
+ * V, token-major with row stride ld) to the ring cache `*c` (host descriptor),
+ * evicting the oldest frames beyond the capacity; when n_frames > capacity only
+ * the last capacity frames are written. Increments c->frames_written by
+ * n_frames at enqueue time (stream order).
+ * Pages: cache of earlier latents' K/V, "Die Schleife" (orcarouter.ai); window of
+ * 18 latent frames and INT8 KV, "Das Single-GPU-Preset" (inferencekey.com).
+ * BF16 cache: plain copy. INT8 cache, per (token, head) vector x of head_dim
+ * values: m = max|x|; s = m/127 (float32, correctly rounded); code =
+ * round-half-even(x/s) (float32 quotient, correctly rounded) clamped to
+ * [-127, 127]; s = 0 and codes 0 when m = 0. Bit-exact by construction.
+ * k_new, v_new: (device) bf16 [n_frames*tpf][ld]; ld >= n_heads*head_dim.
+ */
+int32_t nomas_kvcache_append(nomas_kvcache* c, const uint16_t* k_new, const uint16_t* v_new,
+                             int64_t ld, int32_t n_frames, void* stream);
+
+/* Workspace bytes nomas_segment_attention needs for these sizes and n_splits
+ * (0 = the automatic choice, which depends only on these arguments and on
+ * n_cached, the cached token count at call time). 0 on invalid arguments. */
+size_t nomas_segment_attention_workspace_bytes(int32_t n_video, int32_t n_text, int64_t n_cached,
+                                               int32_t n_heads, int32_t head_dim,
+                                               int32_t n_splits);
+
+/* The split count the call will use for these sizes (n_splits = 0 chooses). */
+int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_text, int64_t n_cached,
+                                       int32_t n_heads, int32_t head_dim, int32_t n_splits);
+
+/*
+ * Block-causal segment attention of the current segment.
+ * Queries: the n_q = n_video + n_text rows of q, video rows first then text.
+ * Keys/values: the retained cache tokens (rows [0, valid_frames*tpf) of each
+ * head of `*c`; INT8 entries enter as code*scale, applied in float32 per key
+ * after an exact int8->bf16 conversion) followed by all n_q rows of k_cur/v_cur.
+ * Every query sees every such key: bidirectional inside the segment, and
+ * earlier segments only through the cache (causal across segments).
+ * out[r, h, :] = sum_j softmax_j(softmax_scale * <q[r,h,:], key_j>) value_j
+ * lse[h*n_q + r] = log sum_j exp(softmax_scale * <q[r,h,:], key_j>) (if lse != NULL)
+ * Pages: "segment-wise causal joint attention", madebyagents.com "Hy-Nomas";
+ * the cache as attention context, orcarouter.ai "Die Schleife".
+ * Arithmetic: bf16 MFMA products, float32 accumulation and softmax; with
+ * n_splits > 1 the key range is cut into that many contiguous chunks whose
+ * partial results are merged by their log-sum-exp in a fixed order (results are
+ * bitwise reproducible run to run for a fixed n_splits).
+ * q, k_cur, v_cur: (device) bf16 [n_q][ld_qkv]; out: (device) bf16
+ * [n_q][ld_out]; lse: (device) float32 [n_heads][n_q] or NULL;
+ * c: (host) descriptor; its n_heads and head_dim are those of q, k_cur, v_cur, out.
+ * softmax_scale > 0 (1/sqrt(head_dim) is the model's). workspace: (device),
+ * 256-byte aligned, >= nomas_segment_attention_workspace_bytes(...).
+ * n_video + n_text >= 1.
+ */
+int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                int64_t ld_qkv, int32_t n_video, int32_t n_text,
+                                const nomas_kvcache* c, uint16_t* out, int64_t ld_out, float* lse,
+                                float softmax_scale, int32_t n_splits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NOMAS_H */

@@ -1,0 +1,63 @@
+"""Build libnomas.so (all HIP kernels + the C ABI) for gfx950 with hipcc.
+
+Run as ``python -m segment_autoregressive_dit_amd.build`` or through
+``__graft_entry__.build()``. The library lands next to this file.
+"""
+
+import os
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libnomas.so")
+SOURCES = ["nomas_host.cpp", "rope3d.hip", "kvcache_append.hip", "attention.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # IEEE float32 division and denormals: the INT8 quantiser is bit-exact only with them
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-fno-fast-math",
+    # no packed-fp32 VALU forms anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose=True, jobs=4):
+    with tempfile.TemporaryDirectory(prefix="nomas_build_") as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            lang = ["-x", "hip"] if src.endswith(".cpp") else []
+            cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+            procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            objs.append(obj)
+        failed = False
+        for src, cmd, p in procs:
+            out = p.communicate()[0].decode()
+            out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+            if p.returncode != 0:
+                failed = True
+                sys.stderr.write(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{out}\n")
+            elif verbose and out.strip():
+                sys.stderr.write(out + "\n")
+        if failed:
+            raise RuntimeError("libnomas build failed")
+        tmp_lib = LIB + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("libnomas link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp_lib, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,226 @@
+"""Thin Python binding of libnomas.so (argument marshalling only).
+
+Every function here has the name of the C entry point it forwards to, and does
+nothing but check tensor dtypes/devices/strides, take device pointers, and pass
+the caller's current HIP stream. All computation happens in the library's HIP
+kernels; there is no fallback: if the library is missing or does not load, the
+first call raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnomas.so")
+
+NOMAS_OK, NOMAS_E_INVALID, NOMAS_E_UNSUPPORTED, NOMAS_E_WORKSPACE, NOMAS_E_HIP = range(5)
+NOMAS_KV_BF16, NOMAS_KV_INT8 = 0, 1
+
+
+class NomasError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[nomas status {code}] {msg}")
+        self.code = code
+
+
+class KVCacheDesc(ctypes.Structure):
+    """Mirror of ``nomas_kvcache`` in include/nomas.h."""
+    _fields_ = [
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("tokens_per_frame", ctypes.c_int32),
+        ("capacity_frames", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("token_pitch", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("frames_written", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libnomas.so once (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m segment_autoregressive_dit_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    desc_p = ctypes.POINTER(KVCacheDesc)
+    sig = {
+        "nomas_version": (i32, []),
+        "nomas_last_error": (ctypes.c_char_p, []),
+        "nomas_kvcache_token_pitch": (i64, [i32, i32]),
+        "nomas_kvcache_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "nomas_kvcache_init": (i32, [desc_p, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "nomas_kvcache_valid_frames": (i64, [desc_p]),
+        "nomas_rope3d": (i32, [vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]),
+        "nomas_kvcache_append": (i32, [desc_p, vp, vp, i64, i32, vp]),
+        "nomas_segment_attention_workspace_bytes": (sz, [i32, i32, i64, i32, i32, i32]),
+        "nomas_segment_attention_splits": (i32, [i32, i32, i64, i32, i32, i32]),
+        "nomas_segment_attention": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(code):
+    if code != NOMAS_OK:
+        raise NomasError(code, lib().nomas_last_error().decode())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _rows_view(t, name, heads, head_dim):
+    """(pointer, row stride) of a bf16 device tensor laid out [rows, ...heads*head_dim]."""
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a bfloat16 CUDA tensor")
+    if t.dim() == 3:
+        if t.shape[1] != heads or t.shape[2] != head_dim or t.stride(2) != 1 or t.stride(1) != head_dim:
+            raise ValueError(f"{name}: expected [rows, {heads}, {head_dim}] with contiguous heads")
+    elif t.dim() == 2:
+        if t.shape[1] < heads * head_dim or t.stride(1) != 1:
+            raise ValueError(f"{name}: expected [rows, >= {heads * head_dim}] with unit inner stride")
+    else:
+        raise ValueError(f"{name}: expected a 2-D or 3-D tensor")
+    return ctypes.c_void_p(t.data_ptr()), t.stride(0)
+
+
+def nomas_version():
+    return lib().nomas_version()
+
+
+def nomas_kvcache_bytes(n_heads, head_dim, tokens_per_frame, capacity_frames, kv_dtype, which):
+    return lib().nomas_kvcache_bytes(n_heads, head_dim, tokens_per_frame, capacity_frames, kv_dtype, which)
+
+
+class KVCache:
+    """Device buffers + descriptor of one layer's ring cache (see nomas_kvcache)."""
+
+    def __init__(self, n_heads, head_dim, tokens_per_frame, capacity_frames, int8, device="cuda"):
+        L = lib()
+        dt = NOMAS_KV_INT8 if int8 else NOMAS_KV_BF16
+        nb = [L.nomas_kvcache_bytes(n_heads, head_dim, tokens_per_frame, capacity_frames, dt, w) for w in range(3)]
+        if nb[0] == 0:
+            _check(L.nomas_kvcache_init(ctypes.byref(KVCacheDesc()), n_heads, head_dim, tokens_per_frame,
+                                        capacity_frames, dt, None, None, None, None))
+        self.k = torch.empty(nb[0], dtype=torch.uint8, device=device)
+        self.v = torch.empty(nb[1], dtype=torch.uint8, device=device)
+        self.k_scale = torch.empty(nb[2] // 4, dtype=torch.float32, device=device) if int8 else None
+        self.v_scale = torch.empty(nb[2] // 4, dtype=torch.float32, device=device) if int8 else None
+        self.desc = KVCacheDesc()
+        _check(L.nomas_kvcache_init(
+            ctypes.byref(self.desc), n_heads, head_dim, tokens_per_frame, capacity_frames, dt,
+            ctypes.c_void_p(self.k.data_ptr()), ctypes.c_void_p(self.v.data_ptr()),
+            ctypes.c_void_p(self.k_scale.data_ptr()) if int8 else None,
+            ctypes.c_void_p(self.v_scale.data_ptr()) if int8 else None))
+        self.int8 = int8
+
+    @property
+    def frames_written(self):
+        return self.desc.frames_written
+
+    @property
+    def valid_frames(self):
+        return lib().nomas_kvcache_valid_frames(ctypes.byref(self.desc))
+
+    @property
+    def token_pitch(self):
+        return self.desc.token_pitch
+
+    @property
+    def n_cached(self):
+        return self.valid_frames * self.desc.tokens_per_frame
+
+    def nomas_kvcache_append(self, k_new, v_new, n_frames, stream=None):
+        d = self.desc
+        kp, ld = _rows_view(k_new, "k_new", d.n_heads, d.head_dim)
+        vp, ldv = _rows_view(v_new, "v_new", d.n_heads, d.head_dim)
+        if ld != ldv:
+            raise ValueError("k_new and v_new must share a row stride")
+        if k_new.shape[0] < n_frames * d.tokens_per_frame or v_new.shape[0] < n_frames * d.tokens_per_frame:
+            raise ValueError("k_new/v_new hold fewer than n_frames*tokens_per_frame rows")
+        _check(lib().nomas_kvcache_append(ctypes.byref(d), kp, vp, ld, n_frames, _stream(stream)))
+
+
+def nomas_rope3d(q, k, t0, n_frames, grid_h, grid_w, band, n_heads, head_dim, theta=10000.0,
+                 inverse=False, stream=None):
+    """Rotate the first n_frames*grid_h*grid_w rows of q (and k) in place."""
+    qp, ld = _rows_view(q, "q", n_heads, head_dim)
+    kp = ctypes.c_void_p(0)
+    if k is not None:
+        kp, ldk = _rows_view(k, "k", n_heads, head_dim)
+        if ldk != ld:
+            raise ValueError("q and k must share a row stride")
+        if k.shape[0] < n_frames * grid_h * grid_w:
+            raise ValueError("k holds fewer rows than the segment's video tokens")
+    if q.shape[0] < n_frames * grid_h * grid_w:
+        raise ValueError("q holds fewer rows than the segment's video tokens")
+    d_t, d_h, d_w = band
+    _check(lib().nomas_rope3d(qp, kp, ld, n_heads, head_dim, t0, n_frames, grid_h, grid_w,
+                              d_t, d_h, d_w, float(theta), int(bool(inverse)), _stream(stream)))
+
+
+def nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, n_splits=0):
+    return lib().nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, n_splits)
+
+
+def nomas_segment_attention_splits(n_video, n_text, n_cached, n_heads, head_dim, n_splits=0):
+    return lib().nomas_segment_attention_splits(n_video, n_text, n_cached, n_heads, head_dim, n_splits)
+
+
+def workspace_for(cache, n_video, n_text, n_splits=0, device="cuda"):
+    d = cache.desc
+    nb = nomas_segment_attention_workspace_bytes(n_video, n_text, cache.n_cached, d.n_heads, d.head_dim, n_splits)
+    return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+
+
+def nomas_segment_attention(q, k_cur, v_cur, n_video, n_text, cache, out=None, lse=None, softmax_scale=None,
+                            n_splits=0, workspace=None, stream=None):
+    """Attention of the current segment's rows against cache + current segment.
+
+    Returns ``out`` ([n_q, H, D] bf16, allocated if not given)."""
+    d = cache.desc
+    H, D = d.n_heads, d.head_dim
+    n_q = n_video + n_text
+    qp, ld = _rows_view(q, "q", H, D)
+    kp, ldk = _rows_view(k_cur, "k_cur", H, D)
+    vp, ldv = _rows_view(v_cur, "v_cur", H, D)
+    if not (ld == ldk == ldv):
+        raise ValueError("q, k_cur, v_cur must share a row stride")
+    for t, name in ((q, "q"), (k_cur, "k_cur"), (v_cur, "v_cur")):
+        if t.shape[0] < n_q:
+            raise ValueError(f"{name} holds fewer than n_video + n_text rows")
+    if out is None:
+        out = torch.empty((n_q, H, D), dtype=torch.bfloat16, device=q.device)
+    op, ldo = _rows_view(out, "out", H, D)
+    if out.shape[0] < n_q:
+        raise ValueError("out holds fewer than n_video + n_text rows")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() < H * n_q:
+            raise ValueError("lse must be a contiguous float32 tensor of n_heads*n_q elements")
+        lp = ctypes.c_void_p(lse.data_ptr())
+    if workspace is None:
+        workspace = workspace_for(cache, n_video, n_text, n_splits, q.device)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().nomas_segment_attention(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d), op, ldo, lp, scale,
+                                         n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                         _stream(stream)))
+    return out

@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol nomas.h
+declares, and rejects invalid arguments on the host before anything is enqueued
+(no call here reaches a kernel launch, so no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from segment_autoregressive_dit_amd import nomas
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "nomas.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nomas_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nomas.lib()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_names_match_the_c_entry_points():
+    for n in ["nomas_rope3d", "nomas_segment_attention", "nomas_segment_attention_workspace_bytes",
+              "nomas_segment_attention_splits", "nomas_kvcache_bytes", "nomas_version"]:
+        assert callable(getattr(nomas, n))
+    assert callable(nomas.KVCache.nomas_kvcache_append)
+
+
+def test_version_and_sizes():
+    L = nomas.lib()
+    assert L.nomas_version() >= 1
+    assert L.nomas_kvcache_token_pitch(960, 18) == 17280            # 135 * 128
+    assert L.nomas_kvcache_token_pitch(880, 18) == 15872            # round_up(15840, 128)
+    assert L.nomas_kvcache_token_pitch(24, 4) == 128
+    assert L.nomas_kvcache_token_pitch(0, 4) == -1
+    pitch = L.nomas_kvcache_token_pitch(960, 18)
+    assert L.nomas_kvcache_bytes(16, 128, 960, 18, 1, 0) == 16 * pitch * 128
+    assert L.nomas_kvcache_bytes(16, 128, 960, 18, 0, 1) == 16 * pitch * 128 * 2
+    assert L.nomas_kvcache_bytes(16, 128, 960, 18, 1, 2) == 16 * pitch * 4
+    assert L.nomas_kvcache_bytes(16, 128, 960, 18, 0, 2) == 0
+    assert L.nomas_kvcache_bytes(16, 96, 960, 18, 0, 0) == 0
+
+
+def _desc(dtype=1, heads=2, dim=64, tpf=24, cap=4):
+    L = nomas.lib()
+    d = nomas.KVCacheDesc()
+    fake = 1 << 20          # 16-byte aligned placeholder addresses, never dereferenced
+    sc = ctypes.c_void_p(fake * 3) if dtype == 1 else None
+    sv = ctypes.c_void_p(fake * 4) if dtype == 1 else None
+    rc = L.nomas_kvcache_init(ctypes.byref(d), heads, dim, tpf, cap, dtype,
+                              ctypes.c_void_p(fake), ctypes.c_void_p(fake * 2), sc, sv)
+    return L, d, rc
+
+
+def test_kvcache_init_validation():
+    L, d, rc = _desc()
+    assert rc == 0 and d.frames_written == 0 and d.token_pitch == 128
+    assert L.nomas_kvcache_valid_frames(ctypes.byref(d)) == 0
+    bad = nomas.KVCacheDesc()
+    f = ctypes.c_void_p(1 << 20)
+    assert L.nomas_kvcache_init(ctypes.byref(bad), 2, 96, 24, 4, 0, f, f, None, None) == nomas.NOMAS_E_UNSUPPORTED
+    assert L.nomas_kvcache_init(ctypes.byref(bad), 2, 64, 24, 4, 1, f, f, None, None) == nomas.NOMAS_E_INVALID
+    assert b"INT8" in L.nomas_last_error()
+    assert L.nomas_kvcache_init(ctypes.byref(bad), 2, 64, 24, 4, 0, ctypes.c_void_p((1 << 20) + 4), f, None,
+                                None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_init(ctypes.byref(bad), 2, 64, 0, 4, 0, f, f, None, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_init(None, 2, 64, 24, 4, 0, f, f, None, None) == nomas.NOMAS_E_INVALID
+
+
+def test_append_rejects_before_launch_and_keeps_descriptor():
+    L, d, _ = _desc()
+    p = ctypes.c_void_p(1 << 24)
+    for args in [(None, p, 128, 2), (p, p, 64, 2), (p, p, 130, 2), (p, p, 128, 0),
+                 (ctypes.c_void_p((1 << 24) + 2), p, 128, 2)]:
+        rc = L.nomas_kvcache_append(ctypes.byref(d), args[0], args[1], args[2], args[3], None)
+        assert rc == nomas.NOMAS_E_INVALID, args
+        assert d.frames_written == 0
+    assert L.nomas_kvcache_append(None, p, p, 128, 1, None) == nomas.NOMAS_E_INVALID
+    d.token_pitch = 64      # corrupted descriptor
+    assert L.nomas_kvcache_append(ctypes.byref(d), p, p, 128, 1, None) == nomas.NOMAS_E_INVALID
+
+
+def test_rope_rejects_before_launch():
+    L = nomas.lib()
+    p = ctypes.c_void_p(1 << 24)
+    ok = dict(q=p, k=p, ld=128, H=2, D=64, t0=0, F=2, gh=4, gw=6, dt=16, dh=24, dw=24, theta=1e4, inv=0)
+    cases = [dict(q=None), dict(D=96), dict(dt=18, dh=24), dict(dt=15, dh=25), dict(dt=16, dh=24, dw=26),
+             dict(F=0), dict(gh=0), dict(t0=-1), dict(theta=0.0), dict(ld=100), dict(ld=127),
+             dict(q=ctypes.c_void_p((1 << 24) + 8))]
+    for c in cases:
+        a = dict(ok, **c)
+        rc = L.nomas_rope3d(a["q"], a["k"], a["ld"], a["H"], a["D"], a["t0"], a["F"], a["gh"], a["gw"], a["dt"],
+                            a["dh"], a["dw"], a["theta"], a["inv"], None)
+        assert rc in (nomas.NOMAS_E_INVALID, nomas.NOMAS_E_UNSUPPORTED), c
+        assert L.nomas_last_error()
+
+
+def test_attention_rejects_before_launch():
+    L, d, _ = _desc()
+    p = ctypes.c_void_p(1 << 24)
+    ws = ctypes.c_void_p(1 << 26)
+    need = L.nomas_segment_attention_workspace_bytes(48, 16, 0, 2, 64, 0)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, ld=128, nv=48, nt=16, out=p, ldo=128, lse=None, scale=0.125, splits=0,
+                 ws=ws, wsb=need)
+        a.update(kw)
+        return L.nomas_segment_attention(a["q"], a["k"], a["v"], a["ld"], a["nv"], a["nt"], ctypes.byref(d),
+                                         a["out"], a["ldo"], a["lse"], a["scale"], a["splits"], a["ws"], a["wsb"],
+                                         None)
+    assert call(q=None) == nomas.NOMAS_E_INVALID
+    assert call(ld=64) == nomas.NOMAS_E_INVALID
+    assert call(ldo=120) == nomas.NOMAS_E_INVALID
+    assert call(nv=0, nt=0) == nomas.NOMAS_E_INVALID
+    assert call(nv=-1) == nomas.NOMAS_E_INVALID
+    assert call(scale=0.0) == nomas.NOMAS_E_INVALID
+    assert call(scale=float("inf")) == nomas.NOMAS_E_INVALID
+    assert call(splits=-2) == nomas.NOMAS_E_INVALID
+    assert call(ws=None) == nomas.NOMAS_E_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 26) + 16)) == nomas.NOMAS_E_WORKSPACE
+    assert call(wsb=need - 1) == nomas.NOMAS_E_WORKSPACE
+    assert b"workspace" in L.nomas_last_error()
+
+
+def test_workspace_and_split_planning():
+    L = nomas.lib()
+    # the measured single-layer shape: 7,680 video + 256 text queries, 17,280 cached
+    s = L.nomas_segment_attention_splits(7680, 256, 17280, 16, 128, 0)
+    assert s >= 1
+    for req in (1, 2, 4, 8):
+        assert L.nomas_segment_attention_splits(7680, 256, 84480, 16, 128, req) == req
+        b1 = L.nomas_segment_attention_workspace_bytes(7680, 256, 84480, 16, 128, req)
+        assert b1 >= 16 * 128 * 7936 * 2 + (req > 1) * req * 16 * 7936 * 128 * 4
+    # more splits than key tiles is clamped
+    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 64, 50) == 1
+    assert L.nomas_segment_attention_workspace_bytes(0, 0, 0, 16, 128, 0) == 0
+    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 96, 0) == -1

@@ -1,0 +1,201 @@
+"""GPU parity of nomas_segment_attention against the fp64 oracle
+(oracle/attention.py), with the cache contents modelled by oracle/ring.py and
+oracle/quant.py. Tolerance for bf16 and INT8 paths vs fp64:
+max|diff| <= 1e-2 * max|ref| and mean|diff| <= 1e-3. For INT8 the reference
+attends to the *dequantised* cache, so the kernel is not charged for the
+quantisation error."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, quant
+from oracle.ring import RingModel
+from segment_autoregressive_dit_amd import nomas, synth
+
+from _gpu_util import dev_bf16, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 1e-3
+
+
+def _prefill(wl, cache, ring, chunk=None, layer=0, ones_v=False):
+    """Append the workload's pre-fill frames (GPU cache and oracle ring model)."""
+    if wl.cached_frames == 0:
+        return
+    kb, vb = synth.prefill_kv(wl, layer)
+    if ones_v:
+        vb = np.full_like(vb, 0x3F80)
+    tpf = wl.tpf
+    chunk = chunk or wl.seg_frames
+    f = 0
+    while f < wl.cached_frames:
+        n = min(chunk, wl.cached_frames - f)
+        sl = slice(f * tpf, (f + n) * tpf)
+        cache.nomas_kvcache_append(dev_bf16(kb[sl]), dev_bf16(vb[sl]), n)
+        ring.append([(kb[(f + i) * tpf:(f + i + 1) * tpf], vb[(f + i) * tpf:(f + i + 1) * tpf]) for i in range(n)])
+        f += n
+
+
+def _past_from_ring(ring, int8):
+    frames = ring.retained()
+    if not frames:
+        return None, None
+    k = np.concatenate([synth.bf16_bits_to_f64(p[0]) for _, p in frames], 0)
+    v = np.concatenate([synth.bf16_bits_to_f64(p[1]) for _, p in frames], 0)
+    if int8:
+        qk, sk = quant.quantise(k)
+        qv, sv = quant.quantise(v)
+        k, v = quant.dequantise(qk, sk), quant.dequantise(qv, sv)
+    return k, v
+
+
+def _check(got, ref, what):
+    diff = np.abs(got - ref)
+    mx, mean, lim = diff.max(), diff.mean(), 1e-2 * np.abs(ref).max()
+    assert mx <= lim and mean <= 1e-3, f"{what}: max|diff| {mx:.3e} (limit {lim:.3e}), mean {mean:.3e}"
+    return mx, mean
+
+
+def _sample_rows(n_q, n_video, rng, extra=24):
+    rows = {0, 1, 15, 16, 127, 128, 255, 256, 511, 512, n_q - 1, max(0, n_video - 1), min(n_q - 1, n_video)}
+    rows |= set(rng.integers(0, n_q, extra).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < n_q))
+
+
+def _run(wl, n_splits=0, full=False, with_lse=True, n_video=None, n_text=None, cached_frames=None,
+         ones_v=False, repeat=1):
+    """Run one attention call of workload ``wl`` on the GPU and check it."""
+    if cached_frames is not None:
+        wl = synth.Workload(**{**wl.__dict__, "cached_frames": cached_frames})
+    H, D = wl.n_heads, wl.head_dim
+    say(f"attention: {wl.name} splits={n_splits} cached={wl.cached_frames} nv={n_video} nt={n_text}")
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, wl.kv_int8)
+    ring = RingModel(wl.capacity_frames)
+    _prefill(wl, cache, ring, ones_v=ones_v)
+    q_bits, k_bits, v_bits = synth.current_qkv(wl)
+    nv = wl.n_video if n_video is None else n_video
+    nt = wl.n_text if n_text is None else n_text
+    rows_all = np.r_[0:nv, wl.n_video:wl.n_video + nt]
+    q_bits, k_bits, v_bits = q_bits[rows_all], k_bits[rows_all], v_bits[rows_all]
+    if ones_v:
+        v_bits = np.full_like(v_bits, 0x3F80)
+    q, k, v = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits)
+    n_q = nv + nt
+    lse = torch.empty(H * n_q, dtype=torch.float32, device="cuda") if with_lse else None
+    outs = []
+    for _ in range(repeat):
+        outs.append(nomas.nomas_segment_attention(q, k, v, nv, nt, cache, lse=lse, n_splits=n_splits))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "results differ between identical calls"
+    got = host_f64(outs[0])
+    kp, vp = _past_from_ring(ring, wl.kv_int8)
+    x = [synth.bf16_bits_to_f64(t) for t in (q_bits, k_bits, v_bits)]
+    scale = 1.0 / math.sqrt(D)
+    if full:
+        rows = np.arange(n_q)
+    else:
+        rows = _sample_rows(n_q, nv, np.random.default_rng(n_q))
+    ref, ref_lse = attention.segment_attention(x[0][rows], x[1], x[2], kp, vp, scale)
+    res = _check(got[rows], ref, wl.name)
+    if with_lse:
+        g_lse = lse.cpu().numpy().reshape(H, n_q)[:, rows]
+        assert np.max(np.abs(g_lse - ref_lse)) <= LSE_TOL, np.max(np.abs(g_lse - ref_lse))
+    return got, res
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_tiny_all_rows(int8):
+    wl = synth.Workload(**{**synth.WORKLOADS["tiny"].__dict__, "kv_int8": int8})
+    _run(wl, full=True, repeat=2)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5])
+def test_tiny_splits(splits):
+    _run(synth.WORKLOADS["tiny"], n_splits=splits, full=True)
+
+
+@pytest.mark.parametrize("case", ["empty_cache", "text_only", "video_only", "one_query", "one_frame_cache"])
+def test_tiny_edge_cases(case):
+    wl = synth.WORKLOADS["tiny"]
+    kw = dict(empty_cache=dict(cached_frames=0), text_only=dict(n_video=0), video_only=dict(n_text=0),
+              one_query=dict(n_video=0, n_text=1), one_frame_cache=dict(cached_frames=1))[case]
+    _run(wl, full=True, **kw)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_ones_values_give_ones(int8):
+    wl = synth.Workload(**{**synth.WORKLOADS["layer_bf16"].__dict__, "kv_int8": int8})
+    got, _ = _run(wl, ones_v=True, with_lse=False)
+    # bf16: exactly representable 1; int8: each cached v is 127 * fp32(1/127)
+    assert np.max(np.abs(got - 1.0)) <= 2.0 ** -7
+
+
+def test_layer_bf16():
+    _run(synth.WORKLOADS["layer_bf16"], repeat=2)
+
+
+def test_layer_int8_outliers():
+    _run(synth.WORKLOADS["layer_int8"], repeat=2)
+
+
+def test_layer_880_ragged():
+    # 22x40 = 880 tokens per frame: ragged cache tail, ragged query tail
+    _run(synth.WORKLOADS["layer_880"])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 8, 0])
+def test_long_history_splits(splits):
+    _run(synth.WORKLOADS["long_bf16"], n_splits=splits)
+
+
+def test_split_results_agree():
+    # every split count gives the same answer to within fp32 merge rounding
+    wl = synth.WORKLOADS["long_bf16"]
+    cache = nomas.KVCache(wl.n_heads, wl.head_dim, wl.tpf, wl.capacity_frames, False)
+    _prefill(wl, cache, RingModel(wl.capacity_frames))
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    say("attention: split agreement")
+    res = [host_f64(nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, n_splits=s))
+           for s in (1, 3, 8)]
+    for r in res[1:]:
+        assert np.max(np.abs(r - res[0])) <= 2.0 ** -6 * np.abs(res[0]).max()
+
+
+def test_session_rope_append_attention():
+    """Four segments through the whole path (RoPE -> attention -> append) with an
+    INT8 window of 3 frames that evicts inside a segment, against the oracle run
+    of the same session (oracle RoPE, quantiser and ring)."""
+    from oracle import formats, rope
+    H, D, gh, gw, F, T, W = 2, 64, 4, 6, 2, 16, 3
+    tpf = gh * gw
+    cache = nomas.KVCache(H, D, tpf, W, True)
+    ring = RingModel(W)
+    for s in range(4):
+        say(f"session segment {s}")
+        n = F * tpf + T
+        qb = synth.normal_bf16((n, H, D), 11, 0, s, 0)
+        kb = synth.normal_bf16((n, H, D), 11, 0, s, 1)
+        vb = synth.normal_bf16((n, H, D), 11, 0, s, 2)
+        q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+        nomas.nomas_rope3d(q, k, s * F, F, gh, gw, (16, 24, 24), H, D)
+        out = nomas.nomas_segment_attention(q, k, v, F * tpf, T, cache)
+        cache.nomas_kvcache_append(k, v, F)
+        # oracle
+        xq, xk, xv = (synth.bf16_bits_to_f64(t) for t in (qb, kb, vb))
+        nv = F * tpf
+        xq[:nv] = formats.to_bf16(rope.rope3d_segment(xq[:nv], s * F, F, gh, gw, 16, 24, 24))
+        xk[:nv] = formats.to_bf16(rope.rope3d_segment(xk[:nv], s * F, F, gh, gw, 16, 24, 24))
+        frames = ring.retained()
+        kp = vp = None
+        if frames:
+            kp = np.concatenate([quant.dequantise(*p[0]) for _, p in frames], 0)
+            vp = np.concatenate([quant.dequantise(*p[1]) for _, p in frames], 0)
+        ref, _ = attention.segment_attention(xq, xk, xv, kp, vp, 1 / math.sqrt(D))
+        _check(host_f64(out), ref, f"session segment {s}")
+        ring.append([(quant.quantise(xk[f * tpf:(f + 1) * tpf]), quant.quantise(xv[f * tpf:(f + 1) * tpf]))
+                     for f in range(F)])

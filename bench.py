@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the segment-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one layer's segment at the full head
+shape (16 x 128 heads, 24x40 latent grid, 18-frame bf16 window = 17,280 cached
+tokens, 8-frame segment = 7,680 video tokens + 256 text tokens):
+    nomas_rope3d(Q, K) -> nomas_segment_attention -> nomas_kvcache_append (8 frames,
+    evicting the 8 oldest, so every step sees the same 18-frame window).
+``value`` = attention FLOP (4 * n_q * n_k * D * H) per step / step time.
+
+Also reported (outside the timed steps):
+  * the attention launch alone (HIP events on the launch stream) against the
+    bf16 MFMA peak -> ``roofline``;
+  * the full denoise sweep: 54 layers x 8 steps x 3 turns of RoPE + attention
+    against per-layer INT8 18-frame windows, with the 54 appends after step 8
+    of each turn -> ``denoise_ms_per_step`` (median over the 24 steps);
+  * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline``.
+Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_layer_bf16_hbm_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "segment_autoregressive_dit_amd", "csrc", "attention.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-denoise", action="store_true", help="skip the 54-layer denoise sweep")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="query rows per head in the CPU sample")
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def layer_step_bench(args):
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["layer_bf16"]
+    H, D, tpf, F = wl.n_heads, wl.head_dim, wl.tpf, wl.seg_frames
+    log(f"[bench] layer step: {wl.n_q} queries x {wl.n_k} keys, {H}x{D} heads, bf16 window {wl.capacity_frames} frames")
+    cache = nomas.KVCache(H, D, tpf, wl.capacity_frames, False)
+    kb, vb = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    qb, kb, vb = synth.current_qkv(wl)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    out = torch.empty_like(q)
+    ws = nomas.workspace_for(cache, wl.n_video, wl.n_text)
+    torch.cuda.synchronize()
+    flop = wl.attention_flop()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        nomas.nomas_rope3d(q, k, wl.t0, F, wl.grid_h, wl.grid_w, wl.rope_split, H, D)
+        if e: e[1].record()
+        nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
+        if e: e[2].record()
+        cache.nomas_kvcache_append(k, v, F)
+        if e: e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rope_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    app_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    res = dict(
+        ms_per_step=wall * 1e3 / args.steps,
+        flop=flop,
+        attn_ms_mean=statistics.mean(attn_ms),
+        attn_ms_median=statistics.median(attn_ms),
+        rope_ms_mean=statistics.mean(rope_ms),
+        append_ms_mean=statistics.mean(app_ms),
+        rope_bytes=2 * 2 * wl.n_video * H * D * 2,             # read + write Q and K video rows
+        append_bytes=2 * wl.n_video * H * D * 2 * 2,           # bf16 window: read K,V + write K,V
+    )
+    log(f"[bench] layer step: {res['ms_per_step']:.3f} ms/step, attention {res['attn_ms_mean']:.3f} ms "
+        f"({flop / res['attn_ms_mean'] / 1e9:.1f} TFLOP/s)")
+    return wl, res
+
+
+def denoise_bench(n_turns=3):
+    """54 layers x 8 Euler steps x n_turns against INT8 18-frame windows."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["denoise_int8"]
+    H, D, tpf, F = wl.n_heads, wl.head_dim, wl.tpf, wl.seg_frames
+    L, S = wl.n_layers, wl.n_steps
+    log(f"[bench] denoise sweep: {L} layers x {S} steps x {n_turns} turns, INT8 window {wl.capacity_frames} frames")
+    g = torch.Generator(device="cuda")
+
+    def randn(shape, seed):
+        g.manual_seed(seed)
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    caches, ws = [], None
+    for layer in range(L):
+        c = nomas.KVCache(H, D, tpf, wl.capacity_frames, True)
+        n = wl.cached_frames * tpf
+        c.nomas_kvcache_append(randn((n, H, D), 1000 * layer + 3), randn((n, H, D), 1000 * layer + 4),
+                               wl.cached_frames)
+        caches.append(c)
+    ws = nomas.workspace_for(caches[0], wl.n_video, wl.n_text)
+    out = torch.empty((wl.n_q, H, D), dtype=torch.bfloat16, device="cuda")
+    step_ms, append_ms = [], []
+    for turn in range(n_turns):
+        qkv = [tuple(randn((wl.n_q, H, D), 1000 * layer + 100 * (turn + 1) + t) for t in range(3))
+               for layer in range(L)]
+        t0 = wl.cached_frames + F * turn
+        torch.cuda.synchronize()
+        for s in range(S):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for layer in range(L):
+                q, k, v = qkv[layer]
+                nomas.nomas_rope3d(q, k, t0, F, wl.grid_h, wl.grid_w, wl.rope_split, H, D)
+                nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, caches[layer], out=out, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            step_ms.append(e0.elapsed_time(e1))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for layer in range(L):
+            caches[layer].nomas_kvcache_append(qkv[layer][1], qkv[layer][2], F)
+        e1.record()
+        torch.cuda.synchronize()
+        append_ms.append(e0.elapsed_time(e1))
+        log(f"[bench] denoise turn {turn + 1}: median step {statistics.median(step_ms[-S:]):.2f} ms, "
+            f"appends {append_ms[-1]:.2f} ms")
+        del qkv
+    flop_step = L * wl.attention_flop()
+    med = statistics.median(step_ms)
+    return dict(denoise_ms_per_step=med, denoise_tflops=flop_step / med / 1e9,
+                denoise_append_ms_per_turn=statistics.mean(append_ms),
+                denoise_int8_append_bytes_per_layer=2 * wl.n_video * H * D * 2 + 2 * wl.n_video * H * D
+                + 2 * wl.n_video * H * 4)
+
+
+def cpu_baseline(rows_per_head):
+    """The fp64 oracle (as it stands) on a bounded sample of the layer workload."""
+    import numpy as np
+    from oracle import attention
+    from segment_autoregressive_dit_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    wl = synth.WORKLOADS["layer_bf16"]
+    q, k, v = (synth.bf16_bits_to_f64(t) for t in synth.current_qkv(wl))
+    kp, vp = (synth.bf16_bits_to_f64(t) for t in synth.prefill_kv(wl))
+    rows = np.linspace(0, wl.n_q - 1, rows_per_head).astype(int)
+    t0 = time.perf_counter()
+    attention.segment_attention(q[rows], k, v, kp, vp, 1.0 / math.sqrt(wl.head_dim))
+    dt = time.perf_counter() - t0
+    flop = 4 * len(rows) * wl.n_k * wl.head_dim * wl.n_heads
+    log(f"[bench] cpu oracle: {len(rows)} rows x {wl.n_heads} heads in {dt:.2f} s")
+    return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{len(rows)} of {wl.n_q} query rows per head, all {wl.n_heads} heads, all {wl.n_k} keys "
+                       f"({flop / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy)")
+
+
+def traffic_per_launch():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    or None when the summary is missing or the kernel source changed since."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if s.get("source_sha256") != src:
+            return None
+        return s["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
+              f"MI355X; sharding across GPUs is described in DESIGN.md, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from segment_autoregressive_dit_amd import nomas
+    nomas.lib()
+
+    wl, r = layer_step_bench(args)
+    value = r["flop"] / (r["ms_per_step"] * 1e-3) / 1e12
+    attn_tflops = r["flop"] / (r["attn_ms_mean"] * 1e-3) / 1e12
+    extra = dict(
+        attention_ms=round(r["attn_ms_mean"], 4),
+        attention_tflops=round(attn_tflops, 1),
+        attention_pct_mfma_peak=round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        rope_us=round(r["rope_ms_mean"] * 1e3, 2),
+        rope_gbps=round(r["rope_bytes"] / (r["rope_ms_mean"] * 1e-3) / 1e9, 1),
+        append_us=round(r["append_ms_mean"] * 1e3, 2),
+        append_gbps=round(r["append_bytes"] / (r["append_ms_mean"] * 1e-3) / 1e9, 1),
+    )
+    if not args.no_denoise:
+        d = denoise_bench()
+        extra.update(denoise_ms_per_step=round(d["denoise_ms_per_step"], 3),
+                     denoise_attention_tflops=round(d["denoise_tflops"], 1),
+                     denoise_append_ms_per_turn=round(d["denoise_append_ms_per_turn"], 3))
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
+    line = {
+        "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single layer, full head shape, bf16 window: 16x128 heads, 24x40 latent grid, "
+                               "18-frame window (17,280 cached tokens), 8-frame segment (7,680 video) + 256 text; "
+                               "step = rope3d + segment attention + cache append",
+                   "n_q": wl.n_q, "n_k": wl.n_k, "heads": wl.n_heads, "head_dim": wl.head_dim,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_per_launch()},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,6 +35,7 @@
 //    share (head, split): they stream the same K/V through that XCD's L2.
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "nomas_common.hpp"
 
@@ -84,6 +85,29 @@ __device__ __forceinline__ int swz_v(int d) {
   return BC == 128 ? (d & 15) : ((d >> 1) & 7);
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap permutes; every lane ends with the same value.
+__device__ __forceinline__ float xmax16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xadd16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xadd32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16 int8 codes -> 16 bf16 (exact: |code| <= 127 < 2^8)
 __device__ __forceinline__ void i8x16_to_bf16(const u32x4 w, u32x4& lo, u32x4& hi) {
 #pragma unroll
@@ -103,48 +127,55 @@ __device__ __forceinline__ void i8x16_to_bf16(const u32x4 w, u32x4& lo, u32x4& h
   }
 }
 
-template <int D, int QB, int NW, int BC, bool I8>
+template <int D, int QB, int NW, int BC, bool I8, bool PIPE>
 struct AttnCfg {
   static constexpr int NT = NW * 64;
-  static constexpr int KC = D / 8;                 // bf16 chunks per K row
-  static constexpr int VC = BC / 8;                // bf16 chunks per V^T row
+  static constexpr int KC = D / 8;                 // 16-byte chunks per K row (bf16)
+  static constexpr int VC = BC / 8;                // 16-byte chunks per V^T row (bf16)
   static constexpr int KT_BYTES = BC * D * 2;
   static constexpr int VT_BYTES = D * BC * 2;
   static constexpr int STAGE = KT_BYTES + VT_BYTES + 2 * BC * 4;
-  static constexpr int NKB = BC * KC / NT;         // bf16 K chunks per thread
-  static constexpr int NVB = D * VC / NT;          // bf16 V chunks per thread
-  static constexpr int NSTG = NKB + NVB;
+  static constexpr int NSTAGES = PIPE ? 3 : 2;
+  static constexpr int NK8 = BC * D / 16 / NT;     // int8 K chunks (16 codes) per thread
+  static constexpr int NV8 = D * BC / 16 / NT;     // int8 V chunks per thread
   static constexpr int BR = NW * QB * 16;          // queries per block
-  static_assert(BC * KC % NT == 0 && D * VC % NT == 0, "tile must split evenly over threads");
-  static_assert(NKB % 2 == 0 && NVB % 2 == 0, "int8 staging uses half the chunks");
+  static constexpr int NKB = BC / 16;              // 16-key blocks of a tile
+  static constexpr int KK = D / 32;                // d-steps of the logit MFMA
+  static constexpr int KI = KT_BYTES / 1024 / NW;  // 1 KB LDS-copy instructions per wave (K)
+  static constexpr int VI = VT_BYTES / 1024 / NW;  // (V^T)
+  static_assert(KT_BYTES % (1024 * NW) == 0 && VT_BYTES % (1024 * NW) == 0, "tile must split into 1 KB copies");
+  static_assert((BC * D / 16) % NT == 0 && NK8 >= 1 && NV8 >= 1, "int8 tile must split evenly over threads");
 };
 
-template <int D, int QB, int NW, int BC, bool I8>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
-  using C = AttnCfg<D, QB, NW, BC, I8>;
-  __shared__ __align__(16) unsigned char lds[2 * C::STAGE];
+template <int D, int QB, int NW, int BC, bool I8, bool PIPE>
+__global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a) {
+  using C = AttnCfg<D, QB, NW, BC, I8, PIPE>;
+  constexpr int NKB = C::NKB, KK = C::KK;
+  constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
+  __shared__ __align__(16) unsigned char lds[C::NSTAGES * C::STAGE];
 
   const int b = blockIdx.x;
   const int logical = (b & 7) * a.per_xcd + (b >> 3);
   if (logical >= a.n_blocks) return;
-  const int qt = logical % a.n_qtiles;
-  const int hs = logical / a.n_qtiles;
-  const int split = hs % a.n_splits;
-  const int h = hs / a.n_splits;
-  const int t_begin = (int)((int64_t)split * a.tiles_total / a.n_splits);
-  const int t_end = (int)((int64_t)(split + 1) * a.tiles_total / a.n_splits);
+  // block -> (query tile, split, head); results pinned to scalar registers
+  const int qt = __builtin_amdgcn_readfirstlane(logical % a.n_qtiles);
+  const int hs = __builtin_amdgcn_readfirstlane(logical / a.n_qtiles);
+  const int split = __builtin_amdgcn_readfirstlane(hs % a.n_splits);
+  const int h = __builtin_amdgcn_readfirstlane(hs / a.n_splits);
+  const int t_begin = __builtin_amdgcn_readfirstlane((int)((int64_t)split * a.tiles_total / a.n_splits));
+  const int t_end = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * a.tiles_total / a.n_splits));
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 4, i16 = lane & 15;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane -> query i16, dims 32kk+8G..+8
-  bf16x8 qf[QB][D / 32];
+  bf16x8 qf[QB][KK];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qt * C::BR + (wave * QB + qb) * 16 + i16;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
       if (row < a.n_q) v = *reinterpret_cast<const u32x4*>(a.q + (int64_t)row * a.ld_qkv + (int64_t)h * D + 32 * kk + 8 * G);
       qf[qb][kk] = __builtin_bit_cast(bf16x8, v);
@@ -161,79 +192,83 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     for (int db = 0; db < D / 16; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 stg[C::NSTG];
+  // ---- buffer descriptors: the range check returns zeros for rows past the valid
+  // cache tokens / the current segment, so those keys' K needs no branch.
+  const __amdgpu_buffer_rsrc_t rk_c = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<char*>(const_cast<void*>(a.kc)) + (int64_t)h * a.pitch_c * D * ES, (short)0, a.n_cached * D * ES, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv_c = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<char*>(const_cast<void*>(a.vc)) + (int64_t)h * D * a.pitch_c * ES, (short)0, D * a.pitch_c * ES, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk_n = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.kcur) + (int64_t)h * D, (short)0, (int)(a.n_cur * a.ld_qkv * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv_n = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.vtcur) + (int64_t)h * D * a.pitch_cur, (short)0, D * a.pitch_cur * 2, 0x00020000);
+
+  // INT8 cache tiles are staged through registers (converted to bf16 on the way
+  // into LDS); every other tile is copied global -> LDS by the load unit itself.
+  u32x4 stg[I8 ? C::NK8 + C::NV8 : 1];
 
   // tile t -> (is cache tile, first key inside its part, valid keys)
   auto tile_info = [&](int t, bool& cache, int& key0, int& nvalid) {
     cache = t < a.tiles_c;
-    if (cache) {
-      key0 = t * BC;
-      nvalid = min(BC, a.n_cached - key0);
-    } else {
-      key0 = (t - a.tiles_c) * BC;
-      nvalid = min(BC, a.n_cur - key0);
-    }
+    key0 = (cache ? t : t - a.tiles_c) * BC;
+    nvalid = min(BC, (cache ? a.n_cached : a.n_cur) - key0);
   };
 
-  // ---- global -> registers
-  auto load_tile = [&](int t) {
+  // ---- issue the loads of tile t into LDS stage st (or into stg for INT8)
+  auto start_tile = [&](int t, int st) {
     bool cache;
     int key0, nvalid;
     tile_info(t, cache, key0, nvalid);
     if (I8 && cache) {
-      const int8_t* kc = static_cast<const int8_t*>(a.kc);
-      const int8_t* vc = static_cast<const int8_t*>(a.vc);
 #pragma unroll
-      for (int j = 0; j < C::NKB / 2; ++j) {
-        const int c = tid + C::NT * j;
-        const int row = c / (D / 16), cc = c % (D / 16);
-        u32x4 v = {0, 0, 0, 0};
-        if (row < nvalid) v = *reinterpret_cast<const u32x4*>(kc + ((int64_t)h * a.pitch_c + key0 + row) * D + cc * 16);
-        stg[j] = v;
+      for (int j = 0; j < C::NK8; ++j) {
+        const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
+        stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rk_c, row * D + cc * 16, key0 * D, 0);
       }
 #pragma unroll
-      for (int j = 0; j < C::NVB / 2; ++j) {
-        const int c = tid + C::NT * j;
-        const int d = c / (BC / 16), cc = c % (BC / 16);
-        stg[C::NKB / 2 + j] = *reinterpret_cast<const u32x4*>(vc + ((int64_t)h * D + d) * a.pitch_c + key0 + cc * 16);
+      for (int j = 0; j < C::NV8; ++j) {
+        const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
+        stg[C::NK8 + j] = __builtin_amdgcn_raw_buffer_load_b128(rv_c, d * a.pitch_c + cc * 16, key0, 0);
       }
     } else {
+      // each wave instruction fills 1 KB of LDS, lane l at byte 16*l; the lane
+      // fetches the global chunk that the swizzled layout puts there
+      const __amdgpu_buffer_rsrc_t rk = cache ? rk_c : rk_n;
+      const __amdgpu_buffer_rsrc_t rv = cache ? rv_c : rv_n;
+      const int kstride = cache ? D * 2 : (int)a.ld_qkv * 2;
+      const int vstride = (cache ? a.pitch_c : a.pitch_cur) * 2;
+      unsigned char* Ks = lds + st * C::STAGE;
+      unsigned char* Vs = Ks + C::KT_BYTES;
 #pragma unroll
-      for (int j = 0; j < C::NKB; ++j) {
-        const int c = tid + C::NT * j;
-        const int row = c / C::KC, cc = c % C::KC;
-        u32x4 v = {0, 0, 0, 0};
-        if (row < nvalid) {
-          const uint16_t* src = cache ? static_cast<const uint16_t*>(a.kc) + ((int64_t)h * a.pitch_c + key0 + row) * D + cc * 8
-                                      : a.kcur + (int64_t)(key0 + row) * a.ld_qkv + (int64_t)h * D + cc * 8;
-          v = *reinterpret_cast<const u32x4*>(src);
-        }
-        stg[j] = v;
+      for (int i = 0; i < C::KI; ++i) {
+        const int blk = wave * C::KI + i, p = blk * 64 + lane;
+        const int row = p / C::KC, c = (p % C::KC) ^ swz_k<D>(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + blk * 1024), 16,
+                                                 row * kstride + c * 16, key0 * kstride, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < C::NVB; ++j) {
-        const int c = tid + C::NT * j;
-        const int d = c / C::VC, cc = c % C::VC;
-        const uint16_t* src = cache ? static_cast<const uint16_t*>(a.vc) + ((int64_t)h * D + d) * a.pitch_c + key0 + cc * 8
-                                    : a.vtcur + ((int64_t)h * D + d) * a.pitch_cur + key0 + cc * 8;
-        stg[C::NKB + j] = *reinterpret_cast<const u32x4*>(src);
+      for (int i = 0; i < C::VI; ++i) {
+        const int blk = wave * C::VI + i, p = blk * 64 + lane;
+        const int d = p / C::VC, c = (p % C::VC) ^ swz_v<BC>(d);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + blk * 1024), 16,
+                                                 d * vstride + c * 16, key0 * 2, 0, 0);
       }
     }
   };
 
-  // ---- registers -> LDS stage (with int8 -> bf16 conversion and key masking)
-  auto store_tile = [&](int t, int stage) {
+  // ---- complete tile t in stage st: INT8 convert + store, or wait for this
+  // wave's copies. A partial tile's values past the end are zeroed afterwards.
+  auto finish_tile = [&](int t, int st) {
     bool cache;
     int key0, nvalid;
     tile_info(t, cache, key0, nvalid);
-    unsigned char* Ks = lds + stage * C::STAGE;
+    unsigned char* Ks = lds + st * C::STAGE;
     unsigned char* Vs = Ks + C::KT_BYTES;
     float* sc = reinterpret_cast<float*>(Vs + C::VT_BYTES);
     if (I8 && cache) {
 #pragma unroll
-      for (int j = 0; j < C::NKB / 2; ++j) {
-        const int c = tid + C::NT * j;
-        const int row = c / (D / 16), cc = c % (D / 16);
+      for (int j = 0; j < C::NK8; ++j) {
+        const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
         u32x4 lo, hi;
         i8x16_to_bf16(stg[j], lo, hi);
         const int s = swz_k<D>(row);
@@ -241,126 +276,135 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
 #pragma unroll
-      for (int j = 0; j < C::NVB / 2; ++j) {
-        const int c = tid + C::NT * j;
-        const int d = c / (BC / 16), cc = c % (BC / 16);
+      for (int j = 0; j < C::NV8; ++j) {
+        const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
         u32x4 lo, hi;
-        i8x16_to_bf16(stg[C::NKB / 2 + j], lo, hi);
-        if (nvalid < BC) {   // zero the codes of keys past the valid range
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k0 = cc * 16 + 2 * e;
-            if (k0 >= nvalid) lo[e] = 0; else if (k0 + 1 >= nvalid) lo[e] &= 0xffffu;
-            const int k1 = cc * 16 + 8 + 2 * e;
-            if (k1 >= nvalid) hi[e] = 0; else if (k1 + 1 >= nvalid) hi[e] &= 0xffffu;
-          }
-        }
+        i8x16_to_bf16(stg[C::NK8 + j], lo, hi);
         const int s = swz_v<BC>(d);
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
-      // scales (0 for keys past the valid range)
       for (int j = tid; j < 2 * BC; j += C::NT) {
         const int kidx = j % BC;
         const float* src = j < BC ? a.ks : a.vs;
         sc[j] = kidx < nvalid ? src[(int64_t)h * a.pitch_c + key0 + kidx] : 0.f;
       }
     } else {
-#pragma unroll
-      for (int j = 0; j < C::NKB; ++j) {
-        const int c = tid + C::NT * j;
-        const int row = c / C::KC, cc = c % C::KC;
-        *reinterpret_cast<u32x4*>(Ks + row * D * 2 + ((cc ^ swz_k<D>(row)) * 16)) = stg[j];
-      }
-#pragma unroll
-      for (int j = 0; j < C::NVB; ++j) {
-        const int c = tid + C::NT * j;
-        const int d = c / C::VC, cc = c % C::VC;
-        u32x4 v = stg[C::NKB + j];
-        if (nvalid < BC) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k0 = cc * 8 + 2 * e;
-            if (k0 >= nvalid) v[e] = 0; else if (k0 + 1 >= nvalid) v[e] &= 0xffffu;
-          }
-        }
-        *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + ((cc ^ swz_v<BC>(d)) * 16)) = v;
-      }
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's global -> LDS copies have landed
     }
   };
 
-  // ---- one tile of MFMA work from an LDS stage
-  auto compute_tile = [&](int t, int stage) {
-    bool cache;
-    int key0, nvalid;
-    tile_info(t, cache, key0, nvalid);
-    const bool scaled = I8 && cache;
-    const unsigned char* Ks = lds + stage * C::STAGE;
-    const unsigned char* Vs = Ks + C::KT_BYTES;
-    const float* sc = reinterpret_cast<const float*>(Vs + C::VT_BYTES);
+  // zero the values of keys past the end of a partial tile (all waves' stores done)
+  auto zero_tail = [&](int st, int nvalid) {
+    unsigned char* Vs = lds + st * C::STAGE + C::KT_BYTES;
+    for (int idx = tid; idx < D * BC; idx += C::NT) {
+      const int d = idx / BC, k = idx % BC;
+      if (k >= nvalid)
+        *reinterpret_cast<uint16_t*>(Vs + d * BC * 2 + (((k >> 3) ^ swz_v<BC>(d)) * 16) + (k & 7) * 2) = 0;
+    }
+  };
 
-    f32x4 s[QB][BC / 32][2];
+  const int krow0 = 8 * (i16 >> 2) + (i16 & 3);   // K row of key block 0 for this lane
+  const int ksw = swz_k<D>(krow0);                 // the same for every key block
+
+  // K fragments of a whole tile (A operands of the logit MFMAs)
+  auto read_keys = [&](int st, bf16x8 (&kf)[KK][NKB]) {
+    const unsigned char* Ks = lds + st * C::STAGE;
 #pragma unroll
-    for (int g = 0; g < BC / 32; ++g) {
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        const int row = 32 * g + 8 * (i16 >> 2) + 4 * bb + (i16 & 3);
-        const int sw = swz_k<D>(row);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
+        kf[kk][kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
+      }
+  };
+  // V^T fragments of a whole tile (A operands of the value MFMAs)
+  auto read_values = [&](int st, bf16x8 (&vf)[BC / 32][D / 16]) {
+    const unsigned char* Vs = lds + st * C::STAGE + C::KT_BYTES;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][g][bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < BC / 32; ++g)
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ sw) * 16));
+      for (int db = 0; db < D / 16; ++db) {
+        const int d = 16 * db + i16;
+        vf[g][db] = *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
+      }
+  };
+
+  // S^T = K Q^T into s (d-steps outermost: QB*NKB independent accumulators);
+  // INT8 keys: logit_j *= k_scale_j (scales of stage st)
+  auto logits_from = [&](int st, const bf16x8 (&kf)[KK][NKB], f32x4 (&s)[QB][NKB], auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][g][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][kk], s[qb][g][bb], 0, 0, 0);
-        }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][kb], qf[qb][kk], s[qb][kb], 0, 0, 0);
+    if constexpr (SCALED) {
+      const float* sc = reinterpret_cast<const float*>(lds + st * C::STAGE + C::KT_BYTES + C::VT_BYTES);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const f32x4 ksv = *reinterpret_cast<const f32x4*>(sc + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] *= ksv;
       }
     }
+  };
+  auto logits = [&](int st, f32x4 (&s)[QB][NKB], auto scaled_tag) {
+    bf16x8 kf[KK][NKB];
+    read_keys(st, kf);
+    logits_from(st, kf, s, scaled_tag);
+  };
 
-    if (scaled) {
+  // keys past the end of a partial tile never win
+  auto mask_tail = [&](f32x4 (&s)[QB][NKB], int nvalid) {
 #pragma unroll
-      for (int g = 0; g < BC / 32; ++g)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const f32x4 ksv = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G + 4 * bb);
+      for (int r = 0; r < 4; ++r)
+        if (32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + r >= nvalid)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][g][bb] *= ksv;
-        }
-    }
-    if (nvalid < BC) {
-#pragma unroll
-      for (int g = 0; g < BC / 32; ++g)
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (32 * g + 8 * G + 4 * bb + r >= nvalid)
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb) s[qb][g][bb][r] = -INFINITY;
-    }
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
+  };
 
-    bf16x8 pf[QB][BC / 32];
+  // tile max per query (all 16 lanes of a query agree), in log2 units
+  auto tile_max = [&](const f32x4 (&s)[QB][NKB], float (&mt)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int g = 0; g < BC / 32; ++g)
+      for (int kb = 0; kb < NKB; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+      mt[qb] = xmax32(xmax16(mx)) * a.c2;
+    }
+  };
+
+  // raise the reference max when a tile exceeds it by more than kTau (rare)
+  auto rescale = [&](const float (&mt)[QB]) {
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qb][g][bb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * a.c2;
-      if (__any(mt > m_ref[qb] + kTau)) {
-        const float mn = fmaxf(m_ref[qb], mt);
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__any(mt[qb] > m_ref[qb] + kTau)) {
+        const float mn = fmaxf(m_ref[qb], mt[qb]);
         const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
         l_sum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) o[qb][db] *= alpha;
         m_ref[qb] = mn;
       }
+    }
+  };
+
+  // P = exp2(c2*s - m_ref) as bf16 MFMA operands; INT8 values: p_j *= v_scale_j
+  auto probs = [&](int st, const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
+    const float* sc = reinterpret_cast<const float*>(lds + st * C::STAGE + C::KT_BYTES + C::VT_BYTES);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_ref[qb];
 #pragma unroll
       for (int g = 0; g < BC / 32; ++g) {
@@ -368,12 +412,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][g][bb][r], a.c2, nm));
-            l_sum[qb] += e;
-            p[4 * bb + r] = e;
-          }
-        if (scaled) {
+          for (int r = 0; r < 4; ++r) p[4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) l_sum[qb] += p[r];
+        if constexpr (SCALED) {
           const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + BC + 32 * g + 8 * G);
           const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + BC + 32 * g + 8 * G + 4);
 #pragma unroll
@@ -388,41 +430,159 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         pf[qb][g] = __builtin_bit_cast(bf16x8, pk);
       }
     }
+  };
 
+  // O^T += V^T P^T
+  auto values_from = [&](const bf16x8 (&vf)[BC / 32][D / 16], const bf16x8 (&pf)[QB][BC / 32]) {
 #pragma unroll
-    for (int g = 0; g < BC / 32; ++g) {
+    for (int g = 0; g < BC / 32; ++g)
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const int d = 16 * db + i16;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
+      for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][g], o[qb][db], 0, 0, 0);
-      }
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g][db], pf[qb][g], o[qb][db], 0, 0, 0);
+  };
+  auto values = [&](int st, const bf16x8 (&pf)[QB][BC / 32]) {
+    bf16x8 vf[BC / 32][D / 16];
+    read_values(st, vf);
+    values_from(vf, pf);
+  };
+
+  // ---- a run of n full tiles [t0, t0+n) of one kind, software-pipelined: the
+  // softmax of tile j and the value MFMAs of tile j share a block with the logit
+  // MFMAs and the row max of tile j+1; LDS holds three tiles (j's values,
+  // j+1's keys, j+2 in flight).
+  auto run_full = [&](int t0, int n, auto scaled_tag) {
+    if (n <= 0) return;
+    start_tile(t0, 0);               // one tile at a time: INT8 tiles share one register stage
+    finish_tile(t0, 0);
+    if (n > 1) {
+      start_tile(t0 + 1, 1);
+      finish_tile(t0 + 1, 1);
+    }
+    __syncthreads();
+    f32x4 scur[QB][NKB];
+    float mt[QB];
+    logits(0, scur, scaled_tag);
+    tile_max(scur, mt);
+    rescale(mt);
+    int st = 0;   // stage of tile t0 + j
+    f32x4 salt[QB][NKB];
+    // one step: tile j (logits in sc_, stage st) and tile j+1 (logits into sn_)
+    auto step = [&](int j, f32x4 (&sc_)[QB][NKB], f32x4 (&sn_)[QB][NKB]) {
+      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+      if (j + 2 < n) start_tile(t0 + j + 2, st2);
+      // phase A: every LDS operand of this step is requested up front
+      bf16x8 kf[KK][NKB];
+      bf16x8 vf[BC / 32][D / 16];
+      read_keys(st1, kf);
+      read_values(st, vf);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase B: softmax of tile j (VALU) beside the logit MFMAs of tile j+1
+      bf16x8 pf[QB][BC / 32];
+      probs(st, sc_, pf, scaled_tag);
+      logits_from(st1, kf, sn_, scaled_tag);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase C: value MFMAs of tile j beside the row max of tile j+1
+      values_from(vf, pf);
+      tile_max(sn_, mt);
+      if (j + 2 < n) finish_tile(t0 + j + 2, st2);
+      __syncthreads();
+      rescale(mt);
+      st = st1;
+    };
+    int j = 0;
+    for (; j + 2 < n; j += 2) {
+      step(j, scur, salt);
+      step(j + 1, salt, scur);
+    }
+    if (j + 1 < n) {
+      step(j, scur, salt);
+      bf16x8 pf[QB][BC / 32];
+      probs(st, salt, pf, scaled_tag);
+      values(st, pf);
+    } else {
+      bf16x8 pf[QB][BC / 32];
+      probs(st, scur, pf, scaled_tag);
+      values(st, pf);
+    }
+    __syncthreads();
+  };
+
+  // ---- a run of n full tiles, unpipelined: LDS double buffer, the next tile's
+  // copies in flight during this tile's MFMAs (two blocks share each CU, so the
+  // other block's waves fill this one's softmax and barrier gaps)
+  auto run_simple = [&](int t0, int n, auto scaled_tag) {
+    if (n <= 0) return;
+    start_tile(t0, 0);
+    finish_tile(t0, 0);
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      const int st = j & 1;
+      const bool more = j + 1 < n;
+      if (more) start_tile(t0 + j + 1, st ^ 1);
+      f32x4 s[QB][NKB];
+      float mt[QB];
+      logits(st, s, scaled_tag);
+      tile_max(s, mt);
+      rescale(mt);
+      bf16x8 pf[QB][BC / 32];
+      probs(st, s, pf, scaled_tag);
+      values(st, pf);
+      if (more) finish_tile(t0 + j + 1, st ^ 1);
+      __syncthreads();
     }
   };
 
-  // ---- main loop: double-buffered LDS, next tile's global loads in flight
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(t_begin, 0);
+  // ---- one partial tile (keys past nvalid masked), unpipelined
+  auto run_partial = [&](int t, auto scaled_tag) {
+    bool cache;
+    int key0, nvalid;
+    tile_info(t, cache, key0, nvalid);
+    start_tile(t, 0);
+    finish_tile(t, 0);
     __syncthreads();
-    for (int t = t_begin; t < t_end; ++t) {
-      const int stage = (t - t_begin) & 1;
-      const bool more = t + 1 < t_end;
-      if (more) load_tile(t + 1);
-      compute_tile(t, stage);
-      if (more) store_tile(t + 1, stage ^ 1);
-      __syncthreads();
-    }
+    zero_tail(0, nvalid);
+    __syncthreads();
+    f32x4 s[QB][NKB];
+    float mt[QB];
+    logits(0, s, scaled_tag);
+    mask_tail(s, nvalid);
+    tile_max(s, mt);
+    rescale(mt);
+    bf16x8 pf[QB][BC / 32];
+    probs(0, s, pf, scaled_tag);
+    values(0, pf);
+    __syncthreads();
+  };
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // this split's tiles: full cache tiles, full current tiles, then the partial
+  // tail of each part (key order does not matter to attention)
+  const int full_c = a.n_cached / BC, full_n = a.n_cur / BC;
+  const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
+  const int n_lo = max(t_begin, a.tiles_c), n_hi = min(t_end, a.tiles_c + full_n);
+  if constexpr (PIPE) {
+    if (I8) run_full(c_lo, c_hi - c_lo, T_{});
+    else run_full(c_lo, c_hi - c_lo, F_{});
+    run_full(n_lo, max(0, n_hi - n_lo), F_{});
+  } else {
+    if (I8) run_simple(c_lo, c_hi - c_lo, T_{});
+    else run_simple(c_lo, c_hi - c_lo, F_{});
+    run_simple(n_lo, max(0, n_hi - n_lo), F_{});
   }
+  if (full_c < a.tiles_c && t_begin <= full_c && full_c < t_end) {
+    if (I8) run_partial(full_c, T_{});
+    else run_partial(full_c, F_{});
+  }
+  const int pn = a.tiles_c + full_n;
+  if (pn < a.tiles_total && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
 
   // ---- epilogue
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float l = l_sum[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = xadd32(xadd16(l_sum[qb]));
     const float inv = 1.0f / l;
     const int row = qt * C::BR + (wave * QB + qb) * 16 + i16;
     if (row >= a.n_q) continue;
@@ -507,8 +667,26 @@ struct Plan {
 
 // Tile shape per head dim: keys per tile, waves per block, 16-query blocks per wave.
 template <int D> struct Shape;
-template <> struct Shape<128> { static constexpr int BC = 64, NW = 8, QB = 2; };
-template <> struct Shape<64> { static constexpr int BC = 64, NW = 4, QB = 2; };
+#ifndef NOMAS_ATTN_BC
+#define NOMAS_ATTN_BC 64
+#endif
+#ifndef NOMAS_ATTN_NW
+#define NOMAS_ATTN_NW 4
+#endif
+#ifndef NOMAS_ATTN_QB
+#define NOMAS_ATTN_QB 2
+#endif
+#ifndef NOMAS_ATTN_PIPE
+#define NOMAS_ATTN_PIPE 0
+#endif
+template <> struct Shape<128> {
+  static constexpr int BC = NOMAS_ATTN_BC, NW = NOMAS_ATTN_NW, QB = NOMAS_ATTN_QB;
+  static constexpr bool PIPE = NOMAS_ATTN_PIPE;
+};
+template <> struct Shape<64> {
+  static constexpr int BC = 64, NW = 4, QB = 2;
+  static constexpr bool PIPE = false;
+};
 constexpr int kCUs = 256;
 static int block_queries(int D) { return D == 128 ? Shape<128>::NW * Shape<128>::QB * 16 : Shape<64>::NW * Shape<64>::QB * 16; }
 static int key_tile(int D) { return D == 128 ? Shape<128>::BC : Shape<64>::BC; }
@@ -555,7 +733,7 @@ template <int D, bool I8>
 static void launch_attn(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(8 * a.per_xcd));
   using S = Shape<D>;
-  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8>), grid, dim3(S::NW * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE>), grid, dim3(S::NW * 64), 0, st, a);
 }
 
 }  // namespace nomas

@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <stddef.h>
 
-#include "../../include/nomas.h"
+#include "nomas.h"
 
 namespace nomas {
 

@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-denoise", action="store_true", help="skip the 54-layer denoise sweep")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="query rows per head in the CPU sample")
+    p.add_argument("--cpu-rows", type=int, default=7936, help="query rows per head in the CPU sample")
     return p.parse_args()
 
 
@@ -209,8 +209,8 @@ def traffic_per_launch():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
-              f"MI355X; sharding across GPUs is described in DESIGN.md, not built).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs on a single "
+              f"MI355X and has no multi-GPU sharding.", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

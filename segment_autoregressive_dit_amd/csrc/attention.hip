@@ -134,8 +134,9 @@ struct AttnCfg {
   static constexpr int VC = BC / 8;                // 16-byte chunks per V^T row (bf16)
   static constexpr int KT_BYTES = BC * D * 2;
   static constexpr int VT_BYTES = D * BC * 2;
-  static constexpr int STAGE = KT_BYTES + VT_BYTES + 2 * BC * 4;
-  static constexpr int NSTAGES = PIPE ? 3 : 2;
+  static constexpr int KSTAGE = KT_BYTES + BC * 4; // K tile + its per-key scales
+  static constexpr int VSTAGE = VT_BYTES + BC * 4; // V^T tile + its per-key scales
+  static constexpr int LDS_BYTES = 2 * (KSTAGE + VSTAGE);
   static constexpr int NK8 = BC * D / 16 / NT;     // int8 K chunks (16 codes) per thread
   static constexpr int NV8 = D * BC / 16 / NT;     // int8 V chunks per thread
   static constexpr int BR = NW * QB * 16;          // queries per block
@@ -148,11 +149,14 @@ struct AttnCfg {
 };
 
 template <int D, int QB, int NW, int BC, bool I8, bool PIPE>
-__global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
   using C = AttnCfg<D, QB, NW, BC, I8, PIPE>;
   constexpr int NKB = C::NKB, KK = C::KK;
   constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
-  __shared__ __align__(16) unsigned char lds[C::NSTAGES * C::STAGE];
+  // two K buffers, then two V^T buffers; tile t lives in buffer t % 2 of each
+  __shared__ __align__(16) unsigned char lds[C::LDS_BYTES];
+  auto kbuf = [&](int i) { return lds + i * C::KSTAGE; };
+  auto vbuf = [&](int i) { return lds + 2 * C::KSTAGE + i * C::VSTAGE; };
 
   const int b = blockIdx.x;
   const int logical = (b & 7) * a.per_xcd + (b >> 3);
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 
   // INT8 cache tiles are staged through registers (converted to bf16 on the way
   // into LDS); every other tile is copied global -> LDS by the load unit itself.
-  u32x4 stg[I8 ? C::NK8 + C::NV8 : 1];
+  u32x4 stk[I8 ? C::NK8 : 1], stv[I8 ? C::NV8 : 1];
 
   // tile t -> (is cache tile, first key inside its part, valid keys)
   auto tile_info = [&](int t, bool& cache, int& key0, int& nvalid) {
@@ -214,8 +218,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     nvalid = min(BC, (cache ? a.n_cached : a.n_cur) - key0);
   };
 
-  // ---- issue the loads of tile t into LDS stage st (or into stg for INT8)
-  auto start_tile = [&](int t, int st) {
+  // ---- issue the loads of tile t's keys / values into K / V buffer i
+  auto start_k = [&](int t, int i) {
     bool cache;
     int key0, nvalid;
     tile_info(t, cache, key0, nvalid);
@@ -223,32 +227,40 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 #pragma unroll
       for (int j = 0; j < C::NK8; ++j) {
         const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
-        stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rk_c, row * D + cc * 16, key0 * D, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < C::NV8; ++j) {
-        const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
-        stg[C::NK8 + j] = __builtin_amdgcn_raw_buffer_load_b128(rv_c, d * a.pitch_c + cc * 16, key0, 0);
+        stk[j] = __builtin_amdgcn_raw_buffer_load_b128(rk_c, row * D + cc * 16, key0 * D, 0);
       }
     } else {
       // each wave instruction fills 1 KB of LDS, lane l at byte 16*l; the lane
       // fetches the global chunk that the swizzled layout puts there
       const __amdgpu_buffer_rsrc_t rk = cache ? rk_c : rk_n;
-      const __amdgpu_buffer_rsrc_t rv = cache ? rv_c : rv_n;
       const int kstride = cache ? D * 2 : (int)a.ld_qkv * 2;
-      const int vstride = (cache ? a.pitch_c : a.pitch_cur) * 2;
-      unsigned char* Ks = lds + st * C::STAGE;
-      unsigned char* Vs = Ks + C::KT_BYTES;
+      unsigned char* Ks = kbuf(i);
 #pragma unroll
-      for (int i = 0; i < C::KI; ++i) {
-        const int blk = wave * C::KI + i, p = blk * 64 + lane;
+      for (int k = 0; k < C::KI; ++k) {
+        const int blk = wave * C::KI + k, p = blk * 64 + lane;
         const int row = p / C::KC, c = (p % C::KC) ^ swz_k<D>(row);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + blk * 1024), 16,
                                                  row * kstride + c * 16, key0 * kstride, 0, 0);
       }
+    }
+  };
+  auto start_v = [&](int t, int i) {
+    bool cache;
+    int key0, nvalid;
+    tile_info(t, cache, key0, nvalid);
+    if (I8 && cache) {
 #pragma unroll
-      for (int i = 0; i < C::VI; ++i) {
-        const int blk = wave * C::VI + i, p = blk * 64 + lane;
+      for (int j = 0; j < C::NV8; ++j) {
+        const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
+        stv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv_c, d * a.pitch_c + cc * 16, key0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rv = cache ? rv_c : rv_n;
+      const int vstride = (cache ? a.pitch_c : a.pitch_cur) * 2;
+      unsigned char* Vs = vbuf(i);
+#pragma unroll
+      for (int k = 0; k < C::VI; ++k) {
+        const int blk = wave * C::VI + k, p = blk * 64 + lane;
         const int d = p / C::VC, c = (p % C::VC) ^ swz_v<BC>(d);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + blk * 1024), 16,
                                                  d * vstride + c * 16, key0 * 2, 0, 0);
@@ -256,47 +268,51 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   };
 
-  // ---- complete tile t in stage st: INT8 convert + store, or wait for this
-  // wave's copies. A partial tile's values past the end are zeroed afterwards.
-  auto finish_tile = [&](int t, int st) {
+  // ---- complete the staging of tile t's keys / values (INT8: convert + store,
+  // with the per-key scales); direct copies are waited for by wait_copies()
+  auto finish_k = [&](int t, int i) {
     bool cache;
     int key0, nvalid;
     tile_info(t, cache, key0, nvalid);
-    unsigned char* Ks = lds + st * C::STAGE;
-    unsigned char* Vs = Ks + C::KT_BYTES;
-    float* sc = reinterpret_cast<float*>(Vs + C::VT_BYTES);
     if (I8 && cache) {
+      unsigned char* Ks = kbuf(i);
 #pragma unroll
       for (int j = 0; j < C::NK8; ++j) {
         const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
         u32x4 lo, hi;
-        i8x16_to_bf16(stg[j], lo, hi);
+        i8x16_to_bf16(stk[j], lo, hi);
         const int s = swz_k<D>(row);
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
+      float* sc = reinterpret_cast<float*>(Ks + C::KT_BYTES);
+      for (int j = tid; j < BC; j += C::NT) sc[j] = j < nvalid ? a.ks[(int64_t)h * a.pitch_c + key0 + j] : 0.f;
+    }
+  };
+  auto finish_v = [&](int t, int i) {
+    bool cache;
+    int key0, nvalid;
+    tile_info(t, cache, key0, nvalid);
+    if (I8 && cache) {
+      unsigned char* Vs = vbuf(i);
 #pragma unroll
       for (int j = 0; j < C::NV8; ++j) {
         const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
         u32x4 lo, hi;
-        i8x16_to_bf16(stg[C::NK8 + j], lo, hi);
+        i8x16_to_bf16(stv[j], lo, hi);
         const int s = swz_v<BC>(d);
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
-      for (int j = tid; j < 2 * BC; j += C::NT) {
-        const int kidx = j % BC;
-        const float* src = j < BC ? a.ks : a.vs;
-        sc[j] = kidx < nvalid ? src[(int64_t)h * a.pitch_c + key0 + kidx] : 0.f;
-      }
-    } else {
-      __builtin_amdgcn_s_waitcnt(0);   // this wave's global -> LDS copies have landed
+      float* sc = reinterpret_cast<float*>(Vs + C::VT_BYTES);
+      for (int j = tid; j < BC; j += C::NT) sc[j] = j < nvalid ? a.vs[(int64_t)h * a.pitch_c + key0 + j] : 0.f;
     }
   };
+  auto wait_copies = [&]() { __builtin_amdgcn_s_waitcnt(0); };
 
-  // zero the values of keys past the end of a partial tile (all waves' stores done)
-  auto zero_tail = [&](int st, int nvalid) {
-    unsigned char* Vs = lds + st * C::STAGE + C::KT_BYTES;
+  // zero the values of keys past the end of a partial tile (all waves' data landed)
+  auto zero_tail = [&](int i, int nvalid) {
+    unsigned char* Vs = vbuf(i);
     for (int idx = tid; idx < D * BC; idx += C::NT) {
       const int d = idx / BC, k = idx % BC;
       if (k >= nvalid)
@@ -307,46 +323,32 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const int krow0 = 8 * (i16 >> 2) + (i16 & 3);   // K row of key block 0 for this lane
   const int ksw = swz_k<D>(krow0);                 // the same for every key block
 
-  // K fragments of a whole tile (A operands of the logit MFMAs)
-  auto read_keys = [&](int st, bf16x8 (&kf)[KK][NKB]) {
-    const unsigned char* Ks = lds + st * C::STAGE;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
-        kf[kk][kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
-      }
-  };
-  // V^T fragments of a whole tile (A operands of the value MFMAs)
-  auto read_values = [&](int st, bf16x8 (&vf)[BC / 32][D / 16]) {
-    const unsigned char* Vs = lds + st * C::STAGE + C::KT_BYTES;
-#pragma unroll
-    for (int g = 0; g < BC / 32; ++g)
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const int d = 16 * db + i16;
-        vf[g][db] = *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
-      }
-  };
-
-  // S^T = K Q^T into s (d-steps outermost: QB*NKB independent accumulators);
-  // INT8 keys: logit_j *= k_scale_j (scales of stage st)
-  auto logits_from = [&](int st, const bf16x8 (&kf)[KK][NKB], f32x4 (&s)[QB][NKB], auto scaled_tag) {
+  // S^T = K Q^T from K buffer i into s (d-steps outermost: QB*NKB independent
+  // accumulators, the d-step's K fragments read just before); INT8 keys:
+  // logit_j *= k_scale_j
+  auto logits = [&](int i, f32x4 (&s)[QB][NKB], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
+    const unsigned char* Ks = kbuf(i);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 kf[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
+        kf[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][kb], qf[qb][kk], s[qb][kb], 0, 0, 0);
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qf[qb][kk], s[qb][kb], 0, 0, 0);
+    }
     if constexpr (SCALED) {
-      const float* sc = reinterpret_cast<const float*>(lds + st * C::STAGE + C::KT_BYTES + C::VT_BYTES);
+      const float* sc = reinterpret_cast<const float*>(Ks + C::KT_BYTES);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const f32x4 ksv = *reinterpret_cast<const f32x4*>(sc + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1));
@@ -354,11 +356,6 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] *= ksv;
       }
     }
-  };
-  auto logits = [&](int st, f32x4 (&s)[QB][NKB], auto scaled_tag) {
-    bf16x8 kf[KK][NKB];
-    read_keys(st, kf);
-    logits_from(st, kf, s, scaled_tag);
   };
 
   // keys past the end of a partial tile never win
@@ -400,9 +397,10 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   };
 
   // P = exp2(c2*s - m_ref) as bf16 MFMA operands; INT8 values: p_j *= v_scale_j
-  auto probs = [&](int st, const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
+  // (scales of V buffer i); the row sum keeps the unscaled p
+  auto probs = [&](int i, const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
-    const float* sc = reinterpret_cast<const float*>(lds + st * C::STAGE + C::KT_BYTES + C::VT_BYTES);
+    const float* sc = reinterpret_cast<const float*>(vbuf(i) + C::VT_BYTES);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_ref[qb];
@@ -416,8 +414,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 #pragma unroll
         for (int r = 0; r < 8; ++r) l_sum[qb] += p[r];
         if constexpr (SCALED) {
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + BC + 32 * g + 8 * G);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + BC + 32 * g + 8 * G + 4);
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G + 4);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             p[r] *= v0[r];
@@ -432,105 +430,107 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   };
 
-  // O^T += V^T P^T
-  auto values_from = [&](const bf16x8 (&vf)[BC / 32][D / 16], const bf16x8 (&pf)[QB][BC / 32]) {
+  // O^T += V^T P^T from V buffer i (one 32-key group's fragments at a time)
+  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32]) {
+    const unsigned char* Vs = vbuf(i);
 #pragma unroll
-    for (int g = 0; g < BC / 32; ++g)
+    for (int g = 0; g < BC / 32; ++g) {
+      bf16x8 vf[D / 16];
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const int d = 16 * db + i16;
+        vf[db] = *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
+      }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g][db], pf[qb][g], o[qb][db], 0, 0, 0);
-  };
-  auto values = [&](int st, const bf16x8 (&pf)[QB][BC / 32]) {
-    bf16x8 vf[BC / 32][D / 16];
-    read_values(st, vf);
-    values_from(vf, pf);
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[qb][g], o[qb][db], 0, 0, 0);
+    }
   };
 
-  // ---- a run of n full tiles [t0, t0+n) of one kind, software-pipelined: the
-  // softmax of tile j and the value MFMAs of tile j share a block with the logit
-  // MFMAs and the row max of tile j+1; LDS holds three tiles (j's values,
-  // j+1's keys, j+2 in flight).
+  // ---- a run of n full tiles [t0, t0+n) of one kind.
+  // PIPE: step j does the softmax and value MFMAs of tile j beside the logit
+  // MFMAs and row max of tile j+1, while K(j+2) and V(j+1) are in flight.
+  // Otherwise: tile by tile, the next tile's copies in flight during its MFMAs.
   auto run_full = [&](int t0, int n, auto scaled_tag) {
     if (n <= 0) return;
-    start_tile(t0, 0);               // one tile at a time: INT8 tiles share one register stage
-    finish_tile(t0, 0);
-    if (n > 1) {
-      start_tile(t0 + 1, 1);
-      finish_tile(t0 + 1, 1);
-    }
-    __syncthreads();
-    f32x4 scur[QB][NKB];
-    float mt[QB];
-    logits(0, scur, scaled_tag);
-    tile_max(scur, mt);
-    rescale(mt);
-    int st = 0;   // stage of tile t0 + j
-    f32x4 salt[QB][NKB];
-    // one step: tile j (logits in sc_, stage st) and tile j+1 (logits into sn_)
-    auto step = [&](int j, f32x4 (&sc_)[QB][NKB], f32x4 (&sn_)[QB][NKB]) {
-      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
-      if (j + 2 < n) start_tile(t0 + j + 2, st2);
-      // phase A: every LDS operand of this step is requested up front
-      bf16x8 kf[KK][NKB];
-      bf16x8 vf[BC / 32][D / 16];
-      read_keys(st1, kf);
-      read_values(st, vf);
-      __builtin_amdgcn_sched_barrier(0);
-      // phase B: softmax of tile j (VALU) beside the logit MFMAs of tile j+1
-      bf16x8 pf[QB][BC / 32];
-      probs(st, sc_, pf, scaled_tag);
-      logits_from(st1, kf, sn_, scaled_tag);
-      __builtin_amdgcn_sched_barrier(0);
-      // phase C: value MFMAs of tile j beside the row max of tile j+1
-      values_from(vf, pf);
-      tile_max(sn_, mt);
-      if (j + 2 < n) finish_tile(t0 + j + 2, st2);
+    if constexpr (PIPE) {
+      start_k(t0, 0);
+      finish_k(t0, 0);
+      start_v(t0, 0);
+      finish_v(t0, 0);
+      if (n > 1) {
+        start_k(t0 + 1, 1);
+        finish_k(t0 + 1, 1);
+      }
+      wait_copies();
       __syncthreads();
-      rescale(mt);
-      st = st1;
-    };
-    int j = 0;
-    for (; j + 2 < n; j += 2) {
-      step(j, scur, salt);
-      step(j + 1, salt, scur);
-    }
-    if (j + 1 < n) {
-      step(j, scur, salt);
-      bf16x8 pf[QB][BC / 32];
-      probs(st, salt, pf, scaled_tag);
-      values(st, pf);
-    } else {
-      bf16x8 pf[QB][BC / 32];
-      probs(st, scur, pf, scaled_tag);
-      values(st, pf);
-    }
-    __syncthreads();
-  };
-
-  // ---- a run of n full tiles, unpipelined: LDS double buffer, the next tile's
-  // copies in flight during this tile's MFMAs (two blocks share each CU, so the
-  // other block's waves fill this one's softmax and barrier gaps)
-  auto run_simple = [&](int t0, int n, auto scaled_tag) {
-    if (n <= 0) return;
-    start_tile(t0, 0);
-    finish_tile(t0, 0);
-    __syncthreads();
-    for (int j = 0; j < n; ++j) {
-      const int st = j & 1;
-      const bool more = j + 1 < n;
-      if (more) start_tile(t0 + j + 1, st ^ 1);
-      f32x4 s[QB][NKB];
+      f32x4 sa[QB][NKB], sb[QB][NKB];
       float mt[QB];
-      logits(st, s, scaled_tag);
-      tile_max(s, mt);
+      logits(0, sa, scaled_tag);
+      tile_max(sa, mt);
       rescale(mt);
+      auto step = [&](int j, f32x4 (&sc_)[QB][NKB], f32x4 (&sn_)[QB][NKB]) {
+        const int i0 = j & 1, i1 = i0 ^ 1;
+        if (j + 2 < n) start_k(t0 + j + 2, i0);
+        start_v(t0 + j + 1, i1);
+        bf16x8 pf[QB][BC / 32];
+        probs(i0, sc_, pf, scaled_tag);
+        logits(i1, sn_, scaled_tag);
+        __builtin_amdgcn_sched_barrier(0);
+        values(i0, pf);
+        tile_max(sn_, mt);
+        if (j + 2 < n) finish_k(t0 + j + 2, i0);
+        finish_v(t0 + j + 1, i1);
+        wait_copies();
+        __syncthreads();
+        rescale(mt);
+      };
+      int j = 0;
+      for (; j + 2 < n; j += 2) {
+        step(j, sa, sb);
+        step(j + 1, sb, sa);
+      }
       bf16x8 pf[QB][BC / 32];
-      probs(st, s, pf, scaled_tag);
-      values(st, pf);
-      if (more) finish_tile(t0 + j + 1, st ^ 1);
+      if (j + 1 < n) {
+        step(j, sa, sb);
+        probs((j + 1) & 1, sb, pf, scaled_tag);
+        values((j + 1) & 1, pf);
+      } else {
+        probs(j & 1, sa, pf, scaled_tag);
+        values(j & 1, pf);
+      }
       __syncthreads();
+    } else {
+      start_k(t0, 0);
+      start_v(t0, 0);
+      finish_k(t0, 0);
+      finish_v(t0, 0);
+      wait_copies();
+      __syncthreads();
+      for (int j = 0; j < n; ++j) {
+        const int i = j & 1;
+        const bool more = j + 1 < n;
+        if (more) {
+          start_k(t0 + j + 1, i ^ 1);
+          start_v(t0 + j + 1, i ^ 1);
+        }
+        f32x4 s[QB][NKB];
+        float mt[QB];
+        logits(i, s, scaled_tag);
+        tile_max(s, mt);
+        rescale(mt);
+        bf16x8 pf[QB][BC / 32];
+        probs(i, s, pf, scaled_tag);
+        values(i, pf);
+        if (more) {
+          finish_k(t0 + j + 1, i ^ 1);
+          finish_v(t0 + j + 1, i ^ 1);
+          wait_copies();
+        }
+        __syncthreads();
+      }
     }
   };
 
@@ -539,8 +539,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     bool cache;
     int key0, nvalid;
     tile_info(t, cache, key0, nvalid);
-    start_tile(t, 0);
-    finish_tile(t, 0);
+    start_k(t, 0);
+    start_v(t, 0);
+    finish_k(t, 0);
+    finish_v(t, 0);
+    wait_copies();
     __syncthreads();
     zero_tail(0, nvalid);
     __syncthreads();
@@ -563,15 +566,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const int full_c = a.n_cached / BC, full_n = a.n_cur / BC;
   const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
   const int n_lo = max(t_begin, a.tiles_c), n_hi = min(t_end, a.tiles_c + full_n);
-  if constexpr (PIPE) {
-    if (I8) run_full(c_lo, c_hi - c_lo, T_{});
-    else run_full(c_lo, c_hi - c_lo, F_{});
-    run_full(n_lo, max(0, n_hi - n_lo), F_{});
-  } else {
-    if (I8) run_simple(c_lo, c_hi - c_lo, T_{});
-    else run_simple(c_lo, c_hi - c_lo, F_{});
-    run_simple(n_lo, max(0, n_hi - n_lo), F_{});
-  }
+  if (I8) run_full(c_lo, c_hi - c_lo, T_{});
+  else run_full(c_lo, c_hi - c_lo, F_{});
+  run_full(n_lo, max(0, n_hi - n_lo), F_{});
   if (full_c < a.tiles_c && t_begin <= full_c && full_c < t_end) {
     if (I8) run_partial(full_c, T_{});
     else run_partial(full_c, F_{});

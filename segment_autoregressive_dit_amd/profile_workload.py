@@ -1,41 +1,48 @@
-"""Profiling driver: run one kernel of the hot path a fixed number of times on a
-named synthetic workload, for use under ``rocprofv3`` (kernel trace or counters).
+"""Profiling driver and rocprofv3 result summarizer.
 
-    python -m segment_autoregressive_dit_amd.profile_workload --kernel attention --workload layer_bf16 --reps 5
-    python -m segment_autoregressive_dit_amd.profile_workload --kernel copy --bytes 1073741824
+Run one kernel of the hot path a fixed number of times on a named synthetic
+workload (for use under ``rocprofv3``)::
 
-``--kernel copy`` runs a plain device-to-device copy of known size (torch's copy
-kernel), the calibration for HBM byte counters (FETCH_SIZE / WRITE_SIZE).
+    python -m segment_autoregressive_dit_amd.profile_workload run --kernel attention --workload layer_bf16 --reps 5
+    python -m segment_autoregressive_dit_amd.profile_workload run --kernel copy --bytes 1073741824
+
+``--kernel copy`` runs a plain streaming kernel of known size (torch's elementwise
+negation of a float32 buffer: reads N bytes, writes N bytes), the calibration for
+the HBM byte counters FETCH_SIZE / WRITE_SIZE.
+
+Summarize rocprofv3 SQLite results (``*_results.db``) into short text files::
+
+    python -m segment_autoregressive_dit_amd.profile_workload trace DB --out FILE.md --command "..."
+    python -m segment_autoregressive_dit_amd.profile_workload traffic --fetch DB --write DB \\
+        --copy-fetch DB --copy-write DB --copy-bytes N --kernel attn_kernel --out FILE.json --command "..."
 """
 
 import argparse
+import collections
+import hashlib
+import json
 import os
+import sqlite3
 import sys
 
-import numpy as np
-import torch
-
-from segment_autoregressive_dit_amd import nomas, synth
+HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def _dev(bits):
+    import numpy as np
+    import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def main(argv=None):
-    p = argparse.ArgumentParser()
-    p.add_argument("--kernel", choices=["attention", "rope", "append", "copy"], required=True)
-    p.add_argument("--workload", default="layer_bf16", choices=sorted(synth.WORKLOADS))
-    p.add_argument("--reps", type=int, default=5)
-    p.add_argument("--splits", type=int, default=0)
-    p.add_argument("--bytes", type=int, default=1 << 30)
-    a = p.parse_args(argv)
+def cmd_run(a):
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
     if a.kernel == "copy":
-        src = torch.empty(a.bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        src = torch.empty(a.bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(a.reps):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         print(f"copy: {a.reps} x {a.bytes} bytes", file=sys.stderr)
         return
@@ -58,6 +65,109 @@ def main(argv=None):
             cache.nomas_kvcache_append(k, v, wl.seg_frames)
     torch.cuda.synchronize()
     print(f"{a.kernel} on {a.workload}: {a.reps} launches", file=sys.stderr)
+
+
+def _kernel_rows(db):
+    con = sqlite3.connect(db)
+    cur = con.cursor()
+    rows = cur.execute("select name, duration from kernels").fetchall()
+    con.close()
+    return rows
+
+
+def cmd_trace(a):
+    rows = _kernel_rows(a.db)
+    agg = collections.OrderedDict()
+    for name, dur in rows:
+        s = agg.setdefault(name, [0, 0.0, float("inf"), 0.0])
+        s[0] += 1
+        s[1] += dur
+        s[2] = min(s[2], dur)
+        s[3] = max(s[3], dur)
+    total = sum(s[1] for s in agg.values())
+    lines = [f"# Kernel trace: {a.title}", "", "Command:", "", "```", a.command, "```", "",
+             "| kernel | calls | total (us) | average (us) | min (us) | max (us) | % |",
+             "|---|---|---|---|---|---|---|"]
+    for name, (n, tot, mn, mx) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {n} | {tot / 1e3:.1f} | {tot / n / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | "
+                     f"{100 * tot / total:.1f} |")
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def _counter_per_dispatch(db, counter, kernel_substr):
+    con = sqlite3.connect(db)
+    cur = con.cursor()
+    rows = cur.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection").fetchall()
+    con.close()
+    per = collections.defaultdict(float)
+    for kn, did, cn, val in rows:
+        if cn == counter and kernel_substr in kn:
+            per[did] += val
+    if not per:
+        raise SystemExit(f"no {counter} values for a kernel matching {kernel_substr!r} in {db}")
+    vals = list(per.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def cmd_traffic(a):
+    fetch, nf = _counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write, nw = _counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    cfetch, _ = _counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
+    cwrite, _ = _counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
+    # counters read KiB per dispatch; a plain copy of N bytes reads N and writes N,
+    # so the calibration factors are (counter KiB * 1024) / N
+    f_fac = cfetch * 1024 / a.copy_bytes
+    w_fac = cwrite * 1024 / a.copy_bytes
+    fetch_b = fetch * 1024 / f_fac
+    write_b = write * 1024 / w_fac
+    src = os.path.join(HERE, "csrc", a.source)
+    out = {
+        "kernel": a.kernel, "workload": a.workload,
+        "fetch_kib_per_dispatch_raw": fetch, "write_kib_per_dispatch_raw": write,
+        "dispatches": [nf, nw],
+        "copy_bytes": a.copy_bytes, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+        "fetch_calibration": f_fac, "write_calibration": w_fac,
+        "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "source": a.source,
+        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "command": a.command,
+    }
+    with open(a.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--kernel", choices=["attention", "rope", "append", "copy"], required=True)
+    r.add_argument("--workload", default="layer_bf16")
+    r.add_argument("--reps", type=int, default=5)
+    r.add_argument("--splits", type=int, default=0)
+    r.add_argument("--bytes", type=int, default=1 << 30)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--out", required=True)
+    t.add_argument("--title", default="")
+    t.add_argument("--command", default="")
+    f = sub.add_parser("traffic")
+    for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--out"):
+        f.add_argument(k, required=True)
+    f.add_argument("--copy-bytes", type=int, required=True)
+    f.add_argument("--kernel", default="attn_kernel")
+    f.add_argument("--copy-kernel", default="elementwise")
+    f.add_argument("--workload", default="layer_bf16")
+    f.add_argument("--source", default="attention.hip")
+    f.add_argument("--command", default="")
+    a = p.parse_args(argv)
+    {"run": cmd_run, "trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
 
 
 if __name__ == "__main__":

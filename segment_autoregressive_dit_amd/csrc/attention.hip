@@ -186,12 +186,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     }
   }
 
+  // O accumulators; row sums of the bf16 probabilities (accumulated by an MFMA
+  // with an all-ones operand, so every lane holds its query's full sum) plus a
+  // VALU-side sum for INT8 tiles, whose probabilities carry the value scales
   f32x4 o[QB][D / 16];
-  float m_ref[QB], l_sum[QB];
+  f32x4 lacc[QB];
+  float m_ref[QB], l_add[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = -INFINITY;
-    l_sum[qb] = 0.f;
+    l_add[qb] = 0.f;
+    lacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
@@ -333,19 +338,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 kf[NKB];
+    // the next d-step's fragments are requested before this step's MFMAs, so the
+    // LDS latency hides behind them (the scheduling barriers keep that order)
+    bf16x8 kf[2][NKB];
+    auto read_k = [&](int kk, bf16x8 (&dst)[NKB]) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
-        kf[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
+        dst[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
       }
+    };
+    read_k(0, kf[0]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) read_k(kk + 1, kf[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qf[qb][kk], s[qb][kb], 0, 0, 0);
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb], qf[qb][kk], s[qb][kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (SCALED) {
       const float* sc = reinterpret_cast<const float*>(Ks + C::KT_BYTES);
@@ -369,69 +382,104 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
           for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
   };
 
-  // tile max per query (all 16 lanes of a query agree), in log2 units
-  auto tile_max = [&](const f32x4 (&s)[QB][NKB], float (&mt)[QB]) {
+  // exact tile max of query block qb (all 16 lanes of a query agree), log2 units
+  auto exact_max = [&](const f32x4 (&s)[QB][NKB], int qb) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-      mt[qb] = xmax32(xmax16(mx)) * a.c2;
-    }
+    for (int kb = 0; kb < NKB; ++kb)
+      mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+    return xmax32(xmax16(mx)) * a.c2;
   };
 
-  // raise the reference max when a tile exceeds it by more than kTau (rare)
-  auto rescale = [&](const float (&mt)[QB]) {
+  // raise the reference max of query block qb to cover tile max mt
+  auto raise_ref = [&](int qb, float mt) {
+    const float mn = fmaxf(m_ref[qb], mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
+    l_add[qb] *= alpha;
+    lacc[qb] *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (__any(mt[qb] > m_ref[qb] + kTau)) {
-        const float mn = fmaxf(m_ref[qb], mt[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
-        l_sum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[qb][db] *= alpha;
-        m_ref[qb] = mn;
-      }
-    }
+    for (int db = 0; db < D / 16; ++db) o[qb][db] *= alpha;
+    m_ref[qb] = mn;
   };
 
-  // P = exp2(c2*s - m_ref) as bf16 MFMA operands; INT8 values: p_j *= v_scale_j
-  // (scales of V buffer i); the row sum keeps the unscaled p
+  // P = exp2(c2*s - m_ref) as bf16 MFMA operands. The probabilities are formed
+  // against the running reference max; when one exceeds 2^kTau (or is not finite,
+  // as on the first tile) the wave raises the reference to the tile max, rescales
+  // O and the sums, and forms them again -- rare after the first tile. Non-negative
+  // bf16 values order like unsigned 16-bit integers, so the check is a packed max.
+  // INT8 values: p_j *= v_scale_j (scales of V buffer i), summed unscaled first.
   auto probs = [&](int i, const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
+    typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+    constexpr unsigned kBig = 0x4380u;   // bf16 pattern of 2^kTau = 256
     const float* sc = reinterpret_cast<const float*>(vbuf(i) + C::VT_BYTES);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float nm = -m_ref[qb];
+      float p[BC / 32][8];
+      u32x4 pk[BC / 32];
+      auto form = [&]() {
+        const float nm = -m_ref[qb];
 #pragma unroll
-      for (int g = 0; g < BC / 32; ++g) {
-        float p[8];
+        for (int g = 0; g < BC / 32; ++g)
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+          for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
+            for (int r = 0; r < 4; ++r) p[g][4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
+      };
+      auto pack = [&]() {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) l_sum[qb] += p[r];
-        if constexpr (SCALED) {
+        for (int g = 0; g < BC / 32; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[g][e] = pack_bf16x2(p[g][2 * e], p[g][2 * e + 1]);
+      };
+      form();
+      bool big;
+      if constexpr (SCALED) {
+        float pm = 0.f;
+#pragma unroll
+        for (int g = 0; g < BC / 32; ++g)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) pm = fmaxf(pm, p[g][r]);
+        big = !(pm <= 256.0f) || m_ref[qb] == -INFINITY;
+      } else {
+        pack();
+        u16x2 mx = {0, 0};
+#pragma unroll
+        for (int g = 0; g < BC / 32; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, pk[g][e]));
+        big = max((unsigned)mx[0], (unsigned)mx[1]) > kBig;
+      }
+      if (__any(big)) {
+        raise_ref(qb, exact_max(s, qb));
+        form();
+        if constexpr (!SCALED) pack();
+      }
+      if constexpr (SCALED) {
+#pragma unroll
+        for (int g = 0; g < BC / 32; ++g) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) l_add[qb] += p[g][r];
           const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G);
           const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G + 4);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            p[r] *= v0[r];
-            p[4 + r] *= v1[r];
+            p[g][r] *= v0[r];
+            p[g][4 + r] *= v1[r];
           }
         }
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-        pf[qb][g] = __builtin_bit_cast(bf16x8, pk);
+        pack();
       }
+#pragma unroll
+      for (int g = 0; g < BC / 32; ++g) pf[qb][g] = __builtin_bit_cast(bf16x8, pk[g]);
     }
   };
 
-  // O^T += V^T P^T from V buffer i (one 32-key group's fragments at a time)
-  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32]) {
+  // O^T += V^T P^T from V buffer i (one 32-key group's fragments at a time);
+  // unscaled tiles also add their row sums with an all-ones A operand
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
     const unsigned char* Vs = vbuf(i);
 #pragma unroll
     for (int g = 0; g < BC / 32; ++g) {
@@ -446,6 +494,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[qb][g], o[qb][db], 0, 0, 0);
+      if constexpr (!SCALED) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][g], lacc[qb], 0, 0, 0);
+      }
     }
   };
 
@@ -467,10 +519,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
       wait_copies();
       __syncthreads();
       f32x4 sa[QB][NKB], sb[QB][NKB];
-      float mt[QB];
       logits(0, sa, scaled_tag);
-      tile_max(sa, mt);
-      rescale(mt);
       auto step = [&](int j, f32x4 (&sc_)[QB][NKB], f32x4 (&sn_)[QB][NKB]) {
         const int i0 = j & 1, i1 = i0 ^ 1;
         if (j + 2 < n) start_k(t0 + j + 2, i0);
@@ -479,13 +528,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
         probs(i0, sc_, pf, scaled_tag);
         logits(i1, sn_, scaled_tag);
         __builtin_amdgcn_sched_barrier(0);
-        values(i0, pf);
-        tile_max(sn_, mt);
+        values(i0, pf, scaled_tag);
         if (j + 2 < n) finish_k(t0 + j + 2, i0);
         finish_v(t0 + j + 1, i1);
         wait_copies();
         __syncthreads();
-        rescale(mt);
       };
       int j = 0;
       for (; j + 2 < n; j += 2) {
@@ -496,10 +543,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
       if (j + 1 < n) {
         step(j, sa, sb);
         probs((j + 1) & 1, sb, pf, scaled_tag);
-        values((j + 1) & 1, pf);
+        values((j + 1) & 1, pf, scaled_tag);
       } else {
         probs(j & 1, sa, pf, scaled_tag);
-        values(j & 1, pf);
+        values(j & 1, pf, scaled_tag);
       }
       __syncthreads();
     } else {
@@ -517,13 +564,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
           start_v(t0 + j + 1, i ^ 1);
         }
         f32x4 s[QB][NKB];
-        float mt[QB];
         logits(i, s, scaled_tag);
-        tile_max(s, mt);
-        rescale(mt);
         bf16x8 pf[QB][BC / 32];
         probs(i, s, pf, scaled_tag);
-        values(i, pf);
+        values(i, pf, scaled_tag);
         if (more) {
           finish_k(t0 + j + 1, i ^ 1);
           finish_v(t0 + j + 1, i ^ 1);
@@ -548,14 +592,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     zero_tail(0, nvalid);
     __syncthreads();
     f32x4 s[QB][NKB];
-    float mt[QB];
     logits(0, s, scaled_tag);
     mask_tail(s, nvalid);
-    tile_max(s, mt);
-    rescale(mt);
     bf16x8 pf[QB][BC / 32];
     probs(0, s, pf, scaled_tag);
-    values(0, pf);
+    values(0, pf, scaled_tag);
     __syncthreads();
   };
 
@@ -579,7 +620,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
   // ---- epilogue
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = xadd32(xadd16(l_sum[qb]));
+    const float l = lacc[qb][0] + xadd32(xadd16(l_add[qb]));
     const float inv = 1.0f / l;
     const int row = qt * C::BR + (wave * QB + qb) * 16 + i16;
     if (row >= a.n_q) continue;

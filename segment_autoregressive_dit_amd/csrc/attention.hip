@@ -44,6 +44,12 @@ namespace nomas {
 int32_t validate_cache(const nomas_kvcache* c, const char* who);
 
 constexpr float kTau = 8.0f;
+
+// wave -> ping-pong group; waves of a block are dealt to the 4 SIMDs round-robin,
+// so with 8 waves, waves w and w+4 share a SIMD and go to different groups
+#ifndef PP_GROUP
+#define PP_GROUP(w) ((w) >> 2)
+#endif
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 
@@ -134,8 +140,8 @@ struct AttnCfg {
   static constexpr int VC = BC / 8;                // 16-byte chunks per V^T row (bf16)
   static constexpr int KT_BYTES = BC * D * 2;
   static constexpr int VT_BYTES = D * BC * 2;
-  static constexpr int KSTAGE = KT_BYTES + BC * 4; // K tile + its per-key scales
-  static constexpr int VSTAGE = VT_BYTES + BC * 4; // V^T tile + its per-key scales
+  static constexpr int KSTAGE = KT_BYTES + 2 * BC * 4; // K tile + the tile's per-key K and V scales
+  static constexpr int VSTAGE = VT_BYTES;          // V^T tile
   static constexpr int LDS_BYTES = 2 * (KSTAGE + VSTAGE);
   static constexpr int NK8 = BC * D / 16 / NT;     // int8 K chunks (16 codes) per thread
   static constexpr int NV8 = D * BC / 16 / NT;     // int8 V chunks per thread
@@ -149,7 +155,7 @@ struct AttnCfg {
 };
 
 template <int D, int QB, int NW, int BC, bool I8, bool PIPE>
-__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a) {
   using C = AttnCfg<D, QB, NW, BC, I8, PIPE>;
   constexpr int NKB = C::NKB, KK = C::KK;
   constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
@@ -290,8 +296,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
+      // the tile's K and V scales travel with its keys (the value scales are
+      // needed by the softmax, which may run before the values are resident)
       float* sc = reinterpret_cast<float*>(Ks + C::KT_BYTES);
-      for (int j = tid; j < BC; j += C::NT) sc[j] = j < nvalid ? a.ks[(int64_t)h * a.pitch_c + key0 + j] : 0.f;
+      for (int j = tid; j < 2 * BC; j += C::NT) {
+        const int kidx = j % BC;
+        const float* src = j < BC ? a.ks : a.vs;
+        sc[j] = kidx < nvalid ? src[(int64_t)h * a.pitch_c + key0 + kidx] : 0.f;
+      }
     }
   };
   auto finish_v = [&](int t, int i) {
@@ -309,8 +321,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
-      float* sc = reinterpret_cast<float*>(Vs + C::VT_BYTES);
-      for (int j = tid; j < BC; j += C::NT) sc[j] = j < nvalid ? a.vs[(int64_t)h * a.pitch_c + key0 + j] : 0.f;
     }
   };
   auto wait_copies = [&]() { __builtin_amdgcn_s_waitcnt(0); };
@@ -331,7 +341,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
   // S^T = K Q^T from K buffer i into s (d-steps outermost: QB*NKB independent
   // accumulators, the d-step's K fragments read just before); INT8 keys:
   // logit_j *= k_scale_j
-  auto logits = [&](int i, f32x4 (&s)[QB][NKB], auto scaled_tag) {
+  auto read_k0 = [&](int i, bf16x8 (&dst)[NKB]) {
+    const unsigned char* Ks = kbuf(i);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
+      dst[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + ((G ^ ksw) * 16));
+    }
+  };
+  // k0: the first d-step's fragments, already requested by the caller
+  auto logits_from = [&](int i, const bf16x8 (&k0)[NKB], f32x4 (&s)[QB][NKB], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
     const unsigned char* Ks = kbuf(i);
 #pragma unroll
@@ -348,7 +367,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
         dst[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
       }
     };
-    read_k(0, kf[0]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kf[0][kb] = k0[kb];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + 1 < KK) read_k(kk + 1, kf[(kk + 1) & 1]);
@@ -369,6 +389,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] *= ksv;
       }
     }
+  };
+
+  auto logits = [&](int i, f32x4 (&s)[QB][NKB], auto scaled_tag) {
+    bf16x8 k0[NKB];
+    read_k0(i, k0);
+    logits_from(i, k0, s, scaled_tag);
   };
 
   // keys past the end of a partial tile never win
@@ -412,7 +438,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
     typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
     constexpr unsigned kBig = 0x4380u;   // bf16 pattern of 2^kTau = 256
-    const float* sc = reinterpret_cast<const float*>(vbuf(i) + C::VT_BYTES);
+    const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES) + BC;   // V scales of tile in K buffer i
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float p[BC / 32][8];
@@ -447,7 +473,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < BC / 32; ++g)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, pk[g][e]));
+          for (int e = 0; e < 4; ++e) {
+            // copy the element first: a bit_cast of the vector element itself
+            // reads element 0 of the vector under this compiler
+            const unsigned w = pk[g][e];
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w));
+          }
         big = max((unsigned)mx[0], (unsigned)mx[1]) > kBig;
       }
       if (__any(big)) {
@@ -475,31 +506,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     }
   };
 
-  // O^T += V^T P^T from V buffer i (one 32-key group's fragments at a time);
-  // unscaled tiles also add their row sums with an all-ones A operand
+  // O^T += V^T P^T from V buffer i; unscaled tiles also add their row sums with
+  // an all-ones A operand. The V fragments of key group g+1 are requested into
+  // the registers of group g as each is consumed, so their LDS latency hides
+  // behind the remaining MFMAs (the scheduling barriers keep that order).
+  // then() runs right after the first group's requests (the caller's next reads).
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
+  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto scaled_tag, auto&& then) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
     const unsigned char* Vs = vbuf(i);
+    auto vread = [&](int g, int db) {
+      const int d = 16 * db + i16;
+      return *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
+    };
+    bf16x8 vf[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) vf[db] = vread(0, db);
+    then();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < BC / 32; ++g) {
-      bf16x8 vf[D / 16];
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const int d = 16 * db + i16;
-        vf[db] = *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
-      }
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[qb][g], o[qb][db], 0, 0, 0);
       if constexpr (!SCALED) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][g], lacc[qb], 0, 0, 0);
       }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[qb][g], o[qb][db], 0, 0, 0);
+        if (g + 1 < BC / 32) vf[db] = vread(g + 1, db);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
+  auto no_reads = []() {};
 
   // ---- a run of n full tiles [t0, t0+n) of one kind.
   // PIPE: step j does the softmax and value MFMAs of tile j beside the logit
@@ -508,47 +549,49 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
   auto run_full = [&](int t0, int n, auto scaled_tag) {
     if (n <= 0) return;
     if constexpr (PIPE) {
+      // Ping-pong: each tile is an MFMA phase H1(t) = [values of t-1, logits of
+      // t] and a VALU phase H2(t) = [softmax of t]. The two wave groups (one wave
+      // of each on every SIMD) run one barrier apart, so in every slot one group
+      // issues MFMAs while the other runs the softmax. Loads of K(s) and V(s-1)
+      // are issued in slot 2s-2 and completed at the end of slot 2s-1.
+      const int grp = PP_GROUP(wave);
+      auto issue = [&](int s) {
+        if (s < n) start_k(t0 + s, s & 1);
+        if (s >= 1 && s - 1 < n) start_v(t0 + s - 1, (s - 1) & 1);
+      };
+      auto complete = [&](int s) {
+        if (s < n) finish_k(t0 + s, s & 1);
+        if (s >= 1 && s - 1 < n) finish_v(t0 + s - 1, (s - 1) & 1);
+        wait_copies();
+      };
       start_k(t0, 0);
       finish_k(t0, 0);
-      start_v(t0, 0);
-      finish_v(t0, 0);
-      if (n > 1) {
-        start_k(t0 + 1, 1);
-        finish_k(t0 + 1, 1);
-      }
       wait_copies();
       __syncthreads();
-      f32x4 sa[QB][NKB], sb[QB][NKB];
-      logits(0, sa, scaled_tag);
-      auto step = [&](int j, f32x4 (&sc_)[QB][NKB], f32x4 (&sn_)[QB][NKB]) {
-        const int i0 = j & 1, i1 = i0 ^ 1;
-        if (j + 2 < n) start_k(t0 + j + 2, i0);
-        start_v(t0 + j + 1, i1);
-        bf16x8 pf[QB][BC / 32];
-        probs(i0, sc_, pf, scaled_tag);
-        logits(i1, sn_, scaled_tag);
-        __builtin_amdgcn_sched_barrier(0);
-        values(i0, pf, scaled_tag);
-        if (j + 2 < n) finish_k(t0 + j + 2, i0);
-        finish_v(t0 + j + 1, i1);
-        wait_copies();
-        __syncthreads();
-      };
-      int j = 0;
-      for (; j + 2 < n; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
-      }
+      f32x4 sacc[QB][NKB];
       bf16x8 pf[QB][BC / 32];
-      if (j + 1 < n) {
-        step(j, sa, sb);
-        probs((j + 1) & 1, sb, pf, scaled_tag);
-        values((j + 1) & 1, pf, scaled_tag);
-      } else {
-        probs(j & 1, sa, pf, scaled_tag);
-        values(j & 1, pf, scaled_tag);
+      if (grp == 1) {     // group B's idle first slot
+        issue(1);
+        __syncthreads();
       }
+      for (int t = 0; t < n; ++t) {
+        // H1(t)
+        if (grp == 0) issue(t + 1);
+        bf16x8 k0[NKB];   // first K fragments of tile t, landing during the value MFMAs
+        if (t >= 1) values((t - 1) & 1, pf, scaled_tag, [&]() { read_k0(t & 1, k0); });
+        else read_k0(t & 1, k0);
+        logits_from(t & 1, k0, sacc, scaled_tag);
+        if (grp == 1) complete(t + 1);
+        __syncthreads();
+        // H2(t)
+        if (grp == 1) issue(t + 2);
+        probs(t & 1, sacc, pf, scaled_tag);
+        if (grp == 0) complete(t + 1);
+        __syncthreads();
+      }
+      values((n - 1) & 1, pf, scaled_tag, no_reads);
       __syncthreads();
+      if (grp == 0) __syncthreads();   // group A's idle last slot
     } else {
       start_k(t0, 0);
       start_v(t0, 0);
@@ -567,7 +610,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
         logits(i, s, scaled_tag);
         bf16x8 pf[QB][BC / 32];
         probs(i, s, pf, scaled_tag);
-        values(i, pf, scaled_tag);
+        values(i, pf, scaled_tag, no_reads);
         if (more) {
           finish_k(t0 + j + 1, i ^ 1);
           finish_v(t0 + j + 1, i ^ 1);
@@ -596,7 +639,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     mask_tail(s, nvalid);
     bf16x8 pf[QB][BC / 32];
     probs(0, s, pf, scaled_tag);
-    values(0, pf, scaled_tag);
+    values(0, pf, scaled_tag, no_reads);
     __syncthreads();
   };
 
@@ -709,13 +752,13 @@ template <int D> struct Shape;
 #define NOMAS_ATTN_BC 64
 #endif
 #ifndef NOMAS_ATTN_NW
-#define NOMAS_ATTN_NW 4
+#define NOMAS_ATTN_NW 8
 #endif
 #ifndef NOMAS_ATTN_QB
 #define NOMAS_ATTN_QB 2
 #endif
 #ifndef NOMAS_ATTN_PIPE
-#define NOMAS_ATTN_PIPE 0
+#define NOMAS_ATTN_PIPE 1
 #endif
 template <> struct Shape<128> {
   static constexpr int BC = NOMAS_ATTN_BC, NW = NOMAS_ATTN_NW, QB = NOMAS_ATTN_QB;
@@ -729,10 +772,13 @@ constexpr int kCUs = 256;
 static int block_queries(int D) { return D == 128 ? Shape<128>::NW * Shape<128>::QB * 16 : Shape<64>::NW * Shape<64>::QB * 16; }
 static int key_tile(int D) { return D == 128 ? Shape<128>::BC : Shape<64>::BC; }
 
-static int auto_splits(int n_qtiles, int H, int tiles_total) {
-  const int blocks = n_qtiles * H;
-  if (blocks >= 2 * kCUs) return 1;
-  int s = (2 * kCUs + blocks - 1) / blocks;
+// resident blocks per CU: the ping-pong schedule runs one 8-wave block per CU
+static int blocks_per_cu(int D) { return (D == 128 ? Shape<128>::PIPE : Shape<64>::PIPE) ? 1 : 2; }
+
+static int auto_splits(int n_qtiles, int H, int tiles_total, int per_cu) {
+  const int blocks = n_qtiles * H, slots = per_cu * kCUs;
+  if (blocks >= slots) return 1;
+  int s = (slots + blocks - 1) / blocks;
   const int max_s = tiles_total / 16;   // at least 16 key tiles per split
   if (s > max_s) s = max_s;
   return s < 1 ? 1 : s;
@@ -751,7 +797,7 @@ static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, i
   p.tiles_c = (int)((n_cached + p.bc - 1) / p.bc);
   p.tiles_total = p.tiles_c + (p.n_q + p.bc - 1) / p.bc;
   p.n_qtiles = (p.n_q + p.br - 1) / p.br;
-  int s = n_splits ? n_splits : auto_splits(p.n_qtiles, H, p.tiles_total);
+  int s = n_splits ? n_splits : auto_splits(p.n_qtiles, H, p.tiles_total, blocks_per_cu(D));
   if (s > p.tiles_total) s = p.tiles_total;
   p.splits = s;
   size_t off = round_up((int64_t)H * D * p.pitch_cur * 2, 256);

@@ -141,3 +141,31 @@ def bf16_bits_to_f64(u):
     """Values of bf16 patterns (widening only: no rounding happens)."""
     u = np.asarray(u).astype(np.uint32) << 16
     return u.view(np.float32).astype(np.float64)
+
+
+def rising_logit_inputs(n_heads, head_dim, n_cached, n_cur, seed, growth_log2=140.0, block=64):
+    """Inputs whose attention logits climb steeply along the key order.
+
+    Every query is a per-head sign pattern u (entries +-1) plus N(0, 0.05^2)
+    noise. In each run of ``block`` consecutive keys (cache keys first, then the
+    current segment's) one key is a_b * u and the others are N(0, 0.05^2) noise,
+    with a_b chosen so that this key's logit (scale 1/sqrt(head_dim), log2 units)
+    grows by about ``growth_log2`` from one run to the next; the key's place in
+    run b is (7b + 3) mod block, so it visits every position class. A running
+    softmax maximum that is not raised on some run overflows exp2 at once.
+    Values are N(0, 1). Returns bf16 patterns (q [n_cur,H,D], k_cache, v_cache
+    [n_cached,H,D], k_cur, v_cur [n_cur,H,D])."""
+    rng = np.random.default_rng(np.random.SeedSequence([9001, seed]))
+    H, D = n_heads, head_dim
+    u = rng.choice(np.array([-1.0, 1.0], np.float32), size=(H, D))
+    q = u[None] + np.float32(0.05) * rng.standard_normal((n_cur, H, D), dtype=np.float32)
+    n_k = n_cached + n_cur
+    k = np.float32(0.05) * rng.standard_normal((n_k, H, D), dtype=np.float32)
+    per_unit = np.sqrt(D) * 1.4426950408889634   # logit of a*u against u, per unit a
+    for b in range((n_k + block - 1) // block):
+        j = b * block + (7 * b + 3) % block
+        if j < n_k:
+            k[j] = np.float32(growth_log2 * (b + 1) / per_unit) * u
+    v = rng.standard_normal((n_k, H, D), dtype=np.float32)
+    kb, vb = _round_bf16_bits(k), _round_bf16_bits(v)
+    return _round_bf16_bits(q), kb[:n_cached], vb[:n_cached], kb[n_cached:], vb[n_cached:]

@@ -203,3 +203,35 @@ def test_session_rope_append_attention():
         _check(host_f64(out), ref, f"session segment {s}")
         ring.append([(quant.quantise(xk[f * tpf:(f + 1) * tpf]), quant.quantise(xv[f * tpf:(f + 1) * tpf]))
                      for f in range(F)])
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_rising_logits_raise_reference(D, int8, splits):
+    """Every 64-key run holds one key whose logit tops all earlier ones by about
+    140 (log2 units), at a position that moves from run to run: each tile must
+    raise the running softmax reference, and a raise missed for any key position
+    overflows the probabilities (inf/NaN output)."""
+    H, tpf, frames, nv, nt = 2, 64, 12, 128, 16
+    n_cached = frames * tpf
+    q_b, kc_b, vc_b, kn_b, vn_b = synth.rising_logit_inputs(H, D, n_cached, nv + nt, seed=D + 2 * int8)
+    say(f"attention: rising logits D={D} int8={int8} splits={splits}")
+    cache = nomas.KVCache(H, D, tpf, frames, int8)
+    cache.nomas_kvcache_append(dev_bf16(kc_b), dev_bf16(vc_b), frames)
+    lse = torch.empty(H * (nv + nt), dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention(dev_bf16(q_b), dev_bf16(kn_b), dev_bf16(vn_b), nv, nt, cache, lse=lse,
+                                        n_splits=splits)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    assert np.all(np.isfinite(got)), "non-finite output: a tile did not raise the softmax reference"
+    kp, vp = synth.bf16_bits_to_f64(kc_b), synth.bf16_bits_to_f64(vc_b)
+    if int8:
+        kp, vp = quant.dequantise(*quant.quantise(kp)), quant.dequantise(*quant.quantise(vp))
+    x = [synth.bf16_bits_to_f64(t) for t in (q_b, kn_b, vn_b)]
+    ref, ref_lse = attention.segment_attention(x[0], x[1], x[2], kp, vp, 1.0 / math.sqrt(D))
+    _check(got, ref, f"rising logits D={D} int8={int8}")
+    g_lse = lse.cpu().numpy().reshape(H, nv + nt)
+    # logits reach ~1.5e3 (natural units): fp32 rounding of the logit itself adds
+    # a few ulp of that size on top of the probability-sum bound
+    assert np.max(np.abs(g_lse - ref_lse)) <= LSE_TOL + 1e-3, np.max(np.abs(g_lse - ref_lse))

@@ -152,16 +152,20 @@ int32_t nomas_rope3d(uint16_t* q, uint16_t* k, int64_t ld, int32_t n_heads, int3
 int32_t nomas_kvcache_append(nomas_kvcache* c, const uint16_t* k_new, const uint16_t* v_new,
                              int64_t ld, int32_t n_frames, void* stream);
 
-/* Workspace bytes nomas_segment_attention needs for these sizes and n_splits
- * (0 = the automatic choice, which depends only on these arguments and on
- * n_cached, the cached token count at call time). 0 on invalid arguments. */
+/* Workspace bytes nomas_segment_attention needs for these sizes, the cache's
+ * kv_dtype (nomas_kv_dtype: it sets the key tile) and n_splits (0 = the
+ * automatic choice, which depends only on these arguments, n_cached being the
+ * cached token count at call time). 0 on invalid arguments. */
 size_t nomas_segment_attention_workspace_bytes(int32_t n_video, int32_t n_text, int64_t n_cached,
-                                               int32_t n_heads, int32_t head_dim,
+                                               int32_t n_heads, int32_t head_dim, int32_t kv_dtype,
                                                int32_t n_splits);
 
-/* The split count the call will use for these sizes (n_splits = 0 chooses). */
+/* The split count the call will use for these sizes (n_splits = 0 chooses; a
+ * request above the number of key tiles is clamped to it). -1 on invalid
+ * arguments. */
 int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_text, int64_t n_cached,
-                                       int32_t n_heads, int32_t head_dim, int32_t n_splits);
+                                       int32_t n_heads, int32_t head_dim, int32_t kv_dtype,
+                                       int32_t n_splits);
 
 /*
  * Block-causal segment attention of the current segment.

@@ -133,7 +133,7 @@ __device__ __forceinline__ void i8x16_to_bf16(const u32x4 w, u32x4& lo, u32x4& h
   }
 }
 
-template <int D, int QB, int NW, int BC, bool I8, bool PIPE>
+template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF>
 struct AttnCfg {
   static constexpr int NT = NW * 64;
   static constexpr int KC = D / 8;                 // 16-byte chunks per K row (bf16)
@@ -142,7 +142,8 @@ struct AttnCfg {
   static constexpr int VT_BYTES = D * BC * 2;
   static constexpr int KSTAGE = KT_BYTES + 2 * BC * 4; // K tile + the tile's per-key K and V scales
   static constexpr int VSTAGE = VT_BYTES;          // V^T tile
-  static constexpr int LDS_BYTES = 2 * (KSTAGE + VSTAGE);
+  static constexpr int NVS = PIPE && VPF ? 3 : 2;  // V^T stages
+  static constexpr int LDS_BYTES = 2 * KSTAGE + NVS * VSTAGE;
   static constexpr int NK8 = BC * D / 16 / NT;     // int8 K chunks (16 codes) per thread
   static constexpr int NV8 = D * BC / 16 / NT;     // int8 V chunks per thread
   static constexpr int BR = NW * QB * 16;          // queries per block
@@ -154,12 +155,12 @@ struct AttnCfg {
   static_assert((BC * D / 16) % NT == 0 && NK8 >= 1 && NV8 >= 1, "int8 tile must split evenly over threads");
 };
 
-template <int D, int QB, int NW, int BC, bool I8, bool PIPE>
+template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF>
 __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a) {
-  using C = AttnCfg<D, QB, NW, BC, I8, PIPE>;
+  using C = AttnCfg<D, QB, NW, BC, I8, PIPE, VPF>;
   constexpr int NKB = C::NKB, KK = C::KK;
   constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
-  // two K buffers, then two V^T buffers; tile t lives in buffer t % 2 of each
+  // two K buffers, then C::NVS V^T buffers
   __shared__ __align__(16) unsigned char lds[C::LDS_BYTES];
   auto kbuf = [&](int i) { return lds + i * C::KSTAGE; };
   auto vbuf = [&](int i) { return lds + 2 * C::KSTAGE + i * C::VSTAGE; };
@@ -338,50 +339,48 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const int krow0 = 8 * (i16 >> 2) + (i16 & 3);   // K row of key block 0 for this lane
   const int ksw = swz_k<D>(krow0);                 // the same for every key block
 
-  // S^T = K Q^T from K buffer i into s (d-steps outermost: QB*NKB independent
-  // accumulators, the d-step's K fragments read just before); INT8 keys:
-  // logit_j *= k_scale_j
-  auto read_k0 = [&](int i, bf16x8 (&dst)[NKB]) {
+  // S^T = K Q^T from K buffer i into s, in steps of KH key blocks x one 32-wide
+  // d-slice (QB*KH independent accumulators per step); each step's K fragments
+  // are requested before the previous step's MFMAs, so the LDS latency hides
+  // behind them (the scheduling barriers keep that order). INT8 keys: logit_j
+  // *= k_scale_j.
+  constexpr int KH = NKB > 4 ? 4 : NKB;
+  constexpr int NSTEP = NKB / KH * KK;
+  auto read_kstep = [&](int i, int st, bf16x8 (&dst)[KH]) {
     const unsigned char* Ks = kbuf(i);
+    const int h = st / KK, kk = st % KK;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int j = 0; j < KH; ++j) {
+      const int kb = h * KH + j;
       const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
-      dst[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + ((G ^ ksw) * 16));
+      dst[j] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
     }
   };
-  // k0: the first d-step's fragments, already requested by the caller
-  auto logits_from = [&](int i, const bf16x8 (&k0)[NKB], f32x4 (&s)[QB][NKB], auto scaled_tag) {
+  auto read_k0 = [&](int i, bf16x8 (&dst)[KH]) { read_kstep(i, 0, dst); };
+  // k0: the first step's fragments, already requested by the caller
+  auto logits_from = [&](int i, const bf16x8 (&k0)[KH], f32x4 (&s)[QB][NKB], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
-    const unsigned char* Ks = kbuf(i);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    // the next d-step's fragments are requested before this step's MFMAs, so the
-    // LDS latency hides behind them (the scheduling barriers keep that order)
-    bf16x8 kf[2][NKB];
-    auto read_k = [&](int kk, bf16x8 (&dst)[NKB]) {
+    bf16x8 kf[2][KH];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int row = krow0 + 32 * (kb >> 1) + 4 * (kb & 1);
-        dst[kb] = *reinterpret_cast<const bf16x8*>(Ks + row * D * 2 + (((4 * kk + G) ^ ksw) * 16));
-      }
-    };
+    for (int j = 0; j < KH; ++j) kf[0][j] = k0[j];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kf[0][kb] = k0[kb];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) read_k(kk + 1, kf[(kk + 1) & 1]);
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + 1 < NSTEP) read_kstep(i, st + 1, kf[(st + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
+      const int h = st / KK, kk = st % KK;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int j = 0; j < KH; ++j)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk & 1][kb], qf[qb][kk], s[qb][kb], 0, 0, 0);
+          s[qb][h * KH + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st & 1][j], qf[qb][kk], s[qb][h * KH + j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (SCALED) {
-      const float* sc = reinterpret_cast<const float*>(Ks + C::KT_BYTES);
+      const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const f32x4 ksv = *reinterpret_cast<const f32x4*>(sc + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1));
@@ -392,7 +391,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   };
 
   auto logits = [&](int i, f32x4 (&s)[QB][NKB], auto scaled_tag) {
-    bf16x8 k0[NKB];
+    bf16x8 k0[KH];
     read_k0(i, k0);
     logits_from(i, k0, s, scaled_tag);
   };
@@ -408,15 +407,6 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
           for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
   };
 
-  // exact tile max of query block qb (all 16 lanes of a query agree), log2 units
-  auto exact_max = [&](const f32x4 (&s)[QB][NKB], int qb) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-    return xmax32(xmax16(mx)) * a.c2;
-  };
-
   // raise the reference max of query block qb to cover tile max mt
   auto raise_ref = [&](int qb, float mt) {
     const float mn = fmaxf(m_ref[qb], mt);
@@ -428,81 +418,49 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     m_ref[qb] = mn;
   };
 
-  // P = exp2(c2*s - m_ref) as bf16 MFMA operands. The probabilities are formed
-  // against the running reference max; when one exceeds 2^kTau (or is not finite,
-  // as on the first tile) the wave raises the reference to the tile max, rescales
-  // O and the sums, and forms them again -- rare after the first tile. Non-negative
-  // bf16 values order like unsigned 16-bit integers, so the check is a packed max.
-  // INT8 values: p_j *= v_scale_j (scales of V buffer i), summed unscaled first.
+  // P = exp2(c2*s - m_ref) as bf16 MFMA operands, against a running reference
+  // max per query that is raised -- O and the sums rescaled -- only when a logit
+  // of the tile exceeds it by more than kTau (always on the first tile, where it
+  // is -inf). Every probability is thus at most 2^kTau, and raises are rare
+  // after the first tile. Each lane tests the maximum of its own logits; a raise
+  // takes the exact tile max over the query's four lanes. INT8 values: the row
+  // sum takes p_j, the MFMA operand p_j * v_scale_j (scales stored beside the
+  // tile's keys in K buffer i).
   auto probs = [&](int i, const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
-    typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
-    constexpr unsigned kBig = 0x4380u;   // bf16 pattern of 2^kTau = 256
-    const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES) + BC;   // V scales of tile in K buffer i
+    const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES) + BC;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float p[BC / 32][8];
-      u32x4 pk[BC / 32];
-      auto form = [&]() {
-        const float nm = -m_ref[qb];
+      float mx = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < BC / 32; ++g)
+      for (int kb = 0; kb < NKB; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+      // NaN (all of this lane's keys masked on a first tile) also raises
+      if (__any(!(fmaf(mx, a.c2, -m_ref[qb]) <= kTau))) raise_ref(qb, xmax32(xmax16(mx)) * a.c2);
+      const float nm = -m_ref[qb];
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb)
+      for (int g = 0; g < BC / 32; ++g) {
+        float p[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[g][4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
-      };
-      auto pack = [&]() {
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int g = 0; g < BC / 32; ++g)
+          for (int r = 0; r < 4; ++r) p[4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
+        if constexpr (SCALED) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pk[g][e] = pack_bf16x2(p[g][2 * e], p[g][2 * e + 1]);
-      };
-      form();
-      bool big;
-      if constexpr (SCALED) {
-        float pm = 0.f;
-#pragma unroll
-        for (int g = 0; g < BC / 32; ++g)
-#pragma unroll
-          for (int r = 0; r < 8; ++r) pm = fmaxf(pm, p[g][r]);
-        big = !(pm <= 256.0f) || m_ref[qb] == -INFINITY;
-      } else {
-        pack();
-        u16x2 mx = {0, 0};
-#pragma unroll
-        for (int g = 0; g < BC / 32; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // copy the element first: a bit_cast of the vector element itself
-            // reads element 0 of the vector under this compiler
-            const unsigned w = pk[g][e];
-            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w));
-          }
-        big = max((unsigned)mx[0], (unsigned)mx[1]) > kBig;
-      }
-      if (__any(big)) {
-        raise_ref(qb, exact_max(s, qb));
-        form();
-        if constexpr (!SCALED) pack();
-      }
-      if constexpr (SCALED) {
-#pragma unroll
-        for (int g = 0; g < BC / 32; ++g) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) l_add[qb] += p[g][r];
+          for (int r = 0; r < 8; ++r) l_add[qb] += p[r];
           const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G);
           const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G + 4);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            p[g][r] *= v0[r];
-            p[g][4 + r] *= v1[r];
+            p[r] *= v0[r];
+            p[4 + r] *= v1[r];
           }
         }
-        pack();
-      }
+        u32x4 w;
 #pragma unroll
-      for (int g = 0; g < BC / 32; ++g) pf[qb][g] = __builtin_bit_cast(bf16x8, pk[g]);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        pf[qb][g] = __builtin_bit_cast(bf16x8, w);
+      }
     }
   };
 
@@ -510,20 +468,18 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // an all-ones A operand. The V fragments of key group g+1 are requested into
   // the registers of group g as each is consumed, so their LDS latency hides
   // behind the remaining MFMAs (the scheduling barriers keep that order).
-  // then() runs right after the first group's requests (the caller's next reads).
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto scaled_tag, auto&& then) {
-    constexpr bool SCALED = decltype(scaled_tag)::value;
-    const unsigned char* Vs = vbuf(i);
-    auto vread = [&](int g, int db) {
-      const int d = 16 * db + i16;
-      return *reinterpret_cast<const bf16x8*>(Vs + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
-    };
-    bf16x8 vf[D / 16];
+  auto vread = [&](int i, int g, int db) {
+    const int d = 16 * db + i16;
+    return *reinterpret_cast<const bf16x8*>(vbuf(i) + d * BC * 2 + (((4 * g + G) ^ swz_v<BC>(d)) * 16));
+  };
+  auto read_v0 = [&](int i, bf16x8 (&vf)[D / 16]) {
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) vf[db] = vread(0, db);
-    then();
-    __builtin_amdgcn_sched_barrier(0);
+    for (int db = 0; db < D / 16; ++db) vf[db] = vread(i, 0, db);
+  };
+  // vf: key group 0's fragments, already requested
+  auto values_from = [&](int i, const bf16x8 (&pf)[QB][BC / 32], bf16x8 (&vf)[D / 16], auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
 #pragma unroll
     for (int g = 0; g < BC / 32; ++g) {
       if constexpr (!SCALED) {
@@ -535,10 +491,18 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[qb][g], o[qb][db], 0, 0, 0);
-        if (g + 1 < BC / 32) vf[db] = vread(g + 1, db);
+        if (g + 1 < BC / 32) vf[db] = vread(i, g + 1, db);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  // then() runs right after the first group's requests (the caller's next reads)
+  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto scaled_tag, auto&& then) {
+    bf16x8 vf[D / 16];
+    read_v0(i, vf);
+    then();
+    __builtin_amdgcn_sched_barrier(0);
+    values_from(i, pf, vf, scaled_tag);
   };
   auto no_reads = []() {};
 
@@ -552,24 +516,33 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       // Ping-pong: each tile is an MFMA phase H1(t) = [values of t-1, logits of
       // t] and a VALU phase H2(t) = [softmax of t]. The two wave groups (one wave
       // of each on every SIMD) run one barrier apart, so in every slot one group
-      // issues MFMAs while the other runs the softmax. Loads of K(s) and V(s-1)
-      // are issued in slot 2s-2 and completed at the end of slot 2s-1.
+      // issues MFMAs while the other runs the softmax. K(s) is issued in slot
+      // 2s-2 and completes at the end of slot 2s-1, into K buffer s%2. V(s)
+      // follows one tile later into V buffer s%2 -- or, with VPF, travels with
+      // K(s) into V buffer s%3, so that each wave's H2(s) can already request
+      // V(s)'s first fragments for its next H1, across the barrier.
       const int grp = PP_GROUP(wave);
+      auto vb = [](int s) { return VPF ? s % 3 : s & 1; };
       auto issue = [&](int s) {
         if (s < n) start_k(t0 + s, s & 1);
-        if (s >= 1 && s - 1 < n) start_v(t0 + s - 1, (s - 1) & 1);
+        const int sv = VPF ? s : s - 1;
+        if (sv >= 0 && sv < n) start_v(t0 + sv, vb(sv));
       };
       auto complete = [&](int s) {
         if (s < n) finish_k(t0 + s, s & 1);
-        if (s >= 1 && s - 1 < n) finish_v(t0 + s - 1, (s - 1) & 1);
+        const int sv = VPF ? s : s - 1;
+        if (sv >= 0 && sv < n) finish_v(t0 + sv, vb(sv));
         wait_copies();
       };
       start_k(t0, 0);
+      if constexpr (VPF) start_v(t0, 0);
       finish_k(t0, 0);
+      if constexpr (VPF) finish_v(t0, 0);
       wait_copies();
       __syncthreads();
       f32x4 sacc[QB][NKB];
       bf16x8 pf[QB][BC / 32];
+      bf16x8 vf[VPF ? D / 16 : 1];
       if (grp == 1) {     // group B's idle first slot
         issue(1);
         __syncthreads();
@@ -577,19 +550,26 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       for (int t = 0; t < n; ++t) {
         // H1(t)
         if (grp == 0) issue(t + 1);
-        bf16x8 k0[NKB];   // first K fragments of tile t, landing during the value MFMAs
-        if (t >= 1) values((t - 1) & 1, pf, scaled_tag, [&]() { read_k0(t & 1, k0); });
-        else read_k0(t & 1, k0);
+        bf16x8 k0[KH];   // first K fragments of tile t, landing during the value MFMAs
+        if constexpr (VPF) {
+          read_k0(t & 1, k0);
+          if (t >= 1) values_from(vb(t - 1), pf, vf, scaled_tag);
+        } else {
+          if (t >= 1) values(vb(t - 1), pf, scaled_tag, [&]() { read_k0(t & 1, k0); });
+          else read_k0(t & 1, k0);
+        }
         logits_from(t & 1, k0, sacc, scaled_tag);
         if (grp == 1) complete(t + 1);
         __syncthreads();
         // H2(t)
         if (grp == 1) issue(t + 2);
         probs(t & 1, sacc, pf, scaled_tag);
+        if constexpr (VPF) read_v0(vb(t), vf);
         if (grp == 0) complete(t + 1);
         __syncthreads();
       }
-      values((n - 1) & 1, pf, scaled_tag, no_reads);
+      if constexpr (VPF) values_from(vb(n - 1), pf, vf, scaled_tag);
+      else values(vb(n - 1), pf, scaled_tag, no_reads);
       __syncthreads();
       if (grp == 0) __syncthreads();   // group A's idle last slot
     } else {
@@ -746,34 +726,32 @@ struct Plan {
   size_t off_part_o, off_part_lse, bytes;
 };
 
-// Tile shape per head dim: keys per tile, waves per block, 16-query blocks per wave.
-template <int D> struct Shape;
+// Tile shape per head dim and cache type: keys per tile, waves per block,
+// 16-query blocks per wave, ping-pong schedule, V prefetch across the barrier
+// (three V stages). INT8 tiles stage through registers, which leaves no room
+// for 128-key tiles in the ping-pong register budget.
+template <int D, bool I8> struct Shape;
 #ifndef NOMAS_ATTN_BC
-#define NOMAS_ATTN_BC 64
+#define NOMAS_ATTN_BC 128
 #endif
-#ifndef NOMAS_ATTN_NW
-#define NOMAS_ATTN_NW 8
-#endif
-#ifndef NOMAS_ATTN_QB
-#define NOMAS_ATTN_QB 2
-#endif
-#ifndef NOMAS_ATTN_PIPE
-#define NOMAS_ATTN_PIPE 1
-#endif
-template <> struct Shape<128> {
-  static constexpr int BC = NOMAS_ATTN_BC, NW = NOMAS_ATTN_NW, QB = NOMAS_ATTN_QB;
-  static constexpr bool PIPE = NOMAS_ATTN_PIPE;
+template <bool I8> struct Shape<128, I8> {
+  static constexpr int BC = I8 ? 64 : NOMAS_ATTN_BC, NW = 8, QB = 2;
+  static constexpr bool PIPE = true, VPF = I8;
 };
-template <> struct Shape<64> {
+template <bool I8> struct Shape<64, I8> {
   static constexpr int BC = 64, NW = 4, QB = 2;
-  static constexpr bool PIPE = false;
+  static constexpr bool PIPE = false, VPF = false;
 };
+static_assert(Shape<128, true>::NW * Shape<128, true>::QB == Shape<128, false>::NW * Shape<128, false>::QB,
+              "both cache types tile the queries alike");
 constexpr int kCUs = 256;
-static int block_queries(int D) { return D == 128 ? Shape<128>::NW * Shape<128>::QB * 16 : Shape<64>::NW * Shape<64>::QB * 16; }
-static int key_tile(int D) { return D == 128 ? Shape<128>::BC : Shape<64>::BC; }
-
+static int block_queries(int D) { return D == 128 ? Shape<128, false>::NW * Shape<128, false>::QB * 16 : Shape<64, false>::NW * Shape<64, false>::QB * 16; }
+static int key_tile(int D, bool i8) {
+  if (D == 128) return i8 ? Shape<128, true>::BC : Shape<128, false>::BC;
+  return i8 ? Shape<64, true>::BC : Shape<64, false>::BC;
+}
 // resident blocks per CU: the ping-pong schedule runs one 8-wave block per CU
-static int blocks_per_cu(int D) { return (D == 128 ? Shape<128>::PIPE : Shape<64>::PIPE) ? 1 : 2; }
+static int blocks_per_cu(int D) { return (D == 128 ? Shape<128, false>::PIPE : Shape<64, false>::PIPE) ? 1 : 2; }
 
 static int auto_splits(int n_qtiles, int H, int tiles_total, int per_cu) {
   const int blocks = n_qtiles * H, slots = per_cu * kCUs;
@@ -784,12 +762,13 @@ static int auto_splits(int n_qtiles, int H, int tiles_total, int per_cu) {
   return s < 1 ? 1 : s;
 }
 
-static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, int n_splits, Plan& p) {
+static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, int kv_dtype, int n_splits,
+                      Plan& p) {
   if (n_video < 0 || n_text < 0 || (int64_t)n_video + n_text < 1 || H < 1 || (D != 64 && D != 128) ||
-      n_cached < 0 || n_splits < 0)
+      n_cached < 0 || n_splits < 0 || (kv_dtype != NOMAS_KV_BF16 && kv_dtype != NOMAS_KV_INT8))
     return false;
   if ((int64_t)n_video + n_text > (1 << 26) || n_cached > ((int64_t)1 << 30)) return false;
-  p.bc = key_tile(D);
+  p.bc = key_tile(D, kv_dtype == NOMAS_KV_INT8);
   p.br = block_queries(D);
   p.n_cached = (int)n_cached;
   p.n_q = n_video + n_text;
@@ -816,8 +795,8 @@ static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, i
 template <int D, bool I8>
 static void launch_attn(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(8 * a.per_xcd));
-  using S = Shape<D>;
-  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE>), grid, dim3(S::NW * 64), 0, st, a);
+  using S = Shape<D, I8>;
+  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE, S::VPF>), grid, dim3(S::NW * 64), 0, st, a);
 }
 
 }  // namespace nomas
@@ -825,16 +804,18 @@ static void launch_attn(const AttnArgs& a, hipStream_t st) {
 using namespace nomas;
 
 extern "C" size_t nomas_segment_attention_workspace_bytes(int32_t n_video, int32_t n_text, int64_t n_cached,
-                                                          int32_t n_heads, int32_t head_dim, int32_t n_splits) {
+                                                          int32_t n_heads, int32_t head_dim, int32_t kv_dtype,
+                                                          int32_t n_splits) {
   Plan p;
-  if (!make_plan(n_video, n_text, n_cached, n_heads, head_dim, n_splits, p)) return 0;
+  if (!make_plan(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype, n_splits, p)) return 0;
   return p.bytes;
 }
 
 extern "C" int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_text, int64_t n_cached,
-                                                  int32_t n_heads, int32_t head_dim, int32_t n_splits) {
+                                                  int32_t n_heads, int32_t head_dim, int32_t kv_dtype,
+                                                  int32_t n_splits) {
   Plan p;
-  if (!make_plan(n_video, n_text, n_cached, n_heads, head_dim, n_splits, p)) return -1;
+  if (!make_plan(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype, n_splits, p)) return -1;
   return p.splits;
 }
 
@@ -857,7 +838,7 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
   if (n_splits < 0) return fail(NOMAS_E_INVALID, "segment_attention: n_splits must be >= 0");
   const int64_t n_cached = nomas_kvcache_valid_frames(c) * c->tokens_per_frame;
   Plan p;
-  if (!make_plan(n_video, n_text, n_cached, H, D, n_splits, p))
+  if (!make_plan(n_video, n_text, n_cached, H, D, c->kv_dtype, n_splits, p))
     return fail(NOMAS_E_INVALID, "segment_attention: sizes out of range");
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(NOMAS_E_WORKSPACE, "segment_attention: workspace must be non-NULL and 256-byte aligned");

@@ -29,13 +29,13 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two floats -> packed bf16x2 (round to nearest even; one v_cvt_pk_bf16_f32 on gfx950).
+// Two floats -> packed bf16x2, round to nearest even: one v_cvt_pk_bf16_f32 on
+// gfx950 (converting the pair as a vector; element-wise casts become one
+// conversion per element plus a v_perm to join them)
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-  bf16x2 v;
-  v[0] = static_cast<__bf16>(lo);
-  v[1] = static_cast<__bf16>(hi);
-  return __builtin_bit_cast(unsigned, v);
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 }  // namespace nomas

@@ -65,8 +65,8 @@ def lib():
         "nomas_kvcache_valid_frames": (i64, [desc_p]),
         "nomas_rope3d": (i32, [vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]),
         "nomas_kvcache_append": (i32, [desc_p, vp, vp, i64, i32, vp]),
-        "nomas_segment_attention_workspace_bytes": (sz, [i32, i32, i64, i32, i32, i32]),
-        "nomas_segment_attention_splits": (i32, [i32, i32, i64, i32, i32, i32]),
+        "nomas_segment_attention_workspace_bytes": (sz, [i32, i32, i64, i32, i32, i32, i32]),
+        "nomas_segment_attention_splits": (i32, [i32, i32, i64, i32, i32, i32, i32]),
         "nomas_segment_attention": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
@@ -177,17 +177,19 @@ def nomas_rope3d(q, k, t0, n_frames, grid_h, grid_w, band, n_heads, head_dim, th
                               d_t, d_h, d_w, float(theta), int(bool(inverse)), _stream(stream)))
 
 
-def nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, n_splits=0):
-    return lib().nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, n_splits)
+def nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype, n_splits=0):
+    return lib().nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype,
+                                                         n_splits)
 
 
-def nomas_segment_attention_splits(n_video, n_text, n_cached, n_heads, head_dim, n_splits=0):
-    return lib().nomas_segment_attention_splits(n_video, n_text, n_cached, n_heads, head_dim, n_splits)
+def nomas_segment_attention_splits(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype, n_splits=0):
+    return lib().nomas_segment_attention_splits(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype, n_splits)
 
 
 def workspace_for(cache, n_video, n_text, n_splits=0, device="cuda"):
     d = cache.desc
-    nb = nomas_segment_attention_workspace_bytes(n_video, n_text, cache.n_cached, d.n_heads, d.head_dim, n_splits)
+    nb = nomas_segment_attention_workspace_bytes(n_video, n_text, cache.n_cached, d.n_heads, d.head_dim, d.kv_dtype,
+                                                 n_splits)
     return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
 
 

@@ -107,7 +107,7 @@ def test_attention_rejects_before_launch():
     L, d, _ = _desc()
     p = ctypes.c_void_p(1 << 24)
     ws = ctypes.c_void_p(1 << 26)
-    need = L.nomas_segment_attention_workspace_bytes(48, 16, 0, 2, 64, 0)
+    need = L.nomas_segment_attention_workspace_bytes(48, 16, 0, 2, 64, d.kv_dtype, 0)
     assert need > 0
 
     def call(**kw):
@@ -133,14 +133,21 @@ def test_attention_rejects_before_launch():
 
 def test_workspace_and_split_planning():
     L = nomas.lib()
+    BF16, INT8 = nomas.NOMAS_KV_BF16, nomas.NOMAS_KV_INT8
     # the measured single-layer shape: 7,680 video + 256 text queries, 17,280 cached
-    s = L.nomas_segment_attention_splits(7680, 256, 17280, 16, 128, 0)
-    assert s >= 1
-    for req in (1, 2, 4, 8):
-        assert L.nomas_segment_attention_splits(7680, 256, 84480, 16, 128, req) == req
-        b1 = L.nomas_segment_attention_workspace_bytes(7680, 256, 84480, 16, 128, req)
-        assert b1 >= 16 * 128 * 7936 * 2 + (req > 1) * req * 16 * 7936 * 128 * 4
-    # more splits than key tiles is clamped
-    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 64, 50) == 1
-    assert L.nomas_segment_attention_workspace_bytes(0, 0, 0, 16, 128, 0) == 0
-    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 96, 0) == -1
+    for dt in (BF16, INT8):
+        s = L.nomas_segment_attention_splits(7680, 256, 17280, 16, 128, dt, 0)
+        assert s >= 1
+        for req in (1, 2, 4, 8):
+            assert L.nomas_segment_attention_splits(7680, 256, 84480, 16, 128, dt, req) == req
+            b1 = L.nomas_segment_attention_workspace_bytes(7680, 256, 84480, 16, 128, dt, req)
+            assert b1 >= 16 * 128 * 7936 * 2 + (req > 1) * req * 16 * 7936 * 128 * 4
+    # more splits than key tiles is clamped (10 current keys: one tile)
+    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 64, BF16, 50) == 1
+    # 1,000 cached + 24 current keys at head dim 128: 8 + 1 tiles of 128 keys
+    # (bf16) or 16 + 1 tiles of 64 keys (INT8)
+    assert L.nomas_segment_attention_splits(16, 8, 1000, 1, 128, BF16, 50) == 9
+    assert L.nomas_segment_attention_splits(16, 8, 1000, 1, 128, INT8, 50) == 17
+    assert L.nomas_segment_attention_workspace_bytes(0, 0, 0, 16, 128, BF16, 0) == 0
+    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 96, BF16, 0) == -1
+    assert L.nomas_segment_attention_splits(10, 0, 0, 1, 64, 7, 0) == -1

@@ -26,9 +26,9 @@
 //  * Online softmax in the log2 domain with a fixed reference max per query that
 //    is only raised when a tile's max exceeds it by more than kTau (probabilities
 //    stay <= 2^kTau, exact in fp32 and bf16 range), so the O rescale is rare.
-//  * INT8 cache tiles: codes are converted to bf16 exactly while staging into
-//    LDS; the key scale multiplies the logit of its key and the value scale
-//    multiplies the probability of its key, both in fp32.
+//  * INT8 cache tiles are staged through registers: key codes are converted to
+//    bf16 exactly and the key scale multiplies the fp32 logit of its key; values
+//    are dequantised (code * scale, rounded once to bf16) on the way into LDS.
 //  * Split-KV: the key tiles are cut into contiguous chunks; each block writes a
 //    normalised fp32 partial and its log-sum-exp, merged in fixed order.
 //  * Block ids are remapped so the blocks that the hardware places on one XCD
@@ -133,6 +133,25 @@ __device__ __forceinline__ void i8x16_to_bf16(const u32x4 w, u32x4& lo, u32x4& h
   }
 }
 
+// 16 int8 codes of 16 consecutive keys -> bf16(code_k * scale_k), one rounding
+__device__ __forceinline__ void i8x16_dequant_bf16(const u32x4 w, const f32x4 (&sc)[4], u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int x = static_cast<int>(w[e]);
+    const float f0 = static_cast<float>((x << 24) >> 24) * sc[e][0];
+    const float f1 = static_cast<float>((x << 16) >> 24) * sc[e][1];
+    const float f2 = static_cast<float>((x << 8) >> 24) * sc[e][2];
+    const float f3 = static_cast<float>(x >> 24) * sc[e][3];
+    if (e < 2) {
+      lo[2 * e] = pack_bf16x2(f0, f1);
+      lo[2 * e + 1] = pack_bf16x2(f2, f3);
+    } else {
+      hi[2 * (e - 2)] = pack_bf16x2(f0, f1);
+      hi[2 * (e - 2) + 1] = pack_bf16x2(f2, f3);
+    }
+  }
+}
+
 template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF>
 struct AttnCfg {
   static constexpr int NT = NW * 64;
@@ -140,7 +159,7 @@ struct AttnCfg {
   static constexpr int VC = BC / 8;                // 16-byte chunks per V^T row (bf16)
   static constexpr int KT_BYTES = BC * D * 2;
   static constexpr int VT_BYTES = D * BC * 2;
-  static constexpr int KSTAGE = KT_BYTES + 2 * BC * 4; // K tile + the tile's per-key K and V scales
+  static constexpr int KSTAGE = KT_BYTES + BC * 4; // K tile + the tile's per-key K scales
   static constexpr int VSTAGE = VT_BYTES;          // V^T tile
   static constexpr int NVS = PIPE && VPF ? 3 : 2;  // V^T stages
   static constexpr int LDS_BYTES = 2 * KSTAGE + NVS * VSTAGE;
@@ -193,16 +212,14 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   }
 
-  // O accumulators; row sums of the bf16 probabilities (accumulated by an MFMA
-  // with an all-ones operand, so every lane holds its query's full sum) plus a
-  // VALU-side sum for INT8 tiles, whose probabilities carry the value scales
+  // O accumulators; row sums of the bf16 probabilities, accumulated by an MFMA
+  // with an all-ones operand, so every lane holds its query's full sum
   f32x4 o[QB][D / 16];
   f32x4 lacc[QB];
-  float m_ref[QB], l_add[QB];
+  float m_ref[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = -INFINITY;
-    l_add[qb] = 0.f;
     lacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -219,9 +236,19 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const __amdgpu_buffer_rsrc_t rv_n = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.vtcur) + (int64_t)h * D * a.pitch_cur, (short)0, D * a.pitch_cur * 2, 0x00020000);
 
-  // INT8 cache tiles are staged through registers (converted to bf16 on the way
-  // into LDS); every other tile is copied global -> LDS by the load unit itself.
+  // per-key scales of the valid cache tokens (zeros beyond: those keys' values
+  // dequantise to 0)
+  const __amdgpu_buffer_rsrc_t rks_c = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.ks) + (int64_t)h * a.pitch_c, (short)0, I8 ? a.n_cached * 4 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rvs_c = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.vs) + (int64_t)h * a.pitch_c, (short)0, I8 ? a.n_cached * 4 : 0, 0x00020000);
+
+  // INT8 cache tiles are staged through registers (codes, plus the scales they
+  // need: one per key for K, sixteen per value chunk); every other tile is
+  // copied global -> LDS by the load unit itself.
   u32x4 stk[I8 ? C::NK8 : 1], stv[I8 ? C::NV8 : 1];
+  float sks = 0.f;
+  f32x4 svs[I8 ? C::NV8 : 1][4];
 
   // tile t -> (is cache tile, first key inside its part, valid keys)
   auto tile_info = [&](int t, bool& cache, int& key0, int& nvalid) {
@@ -241,6 +268,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
         stk[j] = __builtin_amdgcn_raw_buffer_load_b128(rk_c, row * D + cc * 16, key0 * D, 0);
       }
+      if (tid < BC) sks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks_c, tid * 4, key0 * 4, 0));
     } else {
       // each wave instruction fills 1 KB of LDS, lane l at byte 16*l; the lane
       // fetches the global chunk that the swizzled layout puts there
@@ -265,6 +293,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       for (int j = 0; j < C::NV8; ++j) {
         const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
         stv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv_c, d * a.pitch_c + cc * 16, key0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          svs[j][e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs_c, (cc * 16 + 4 * e) * 4, key0 * 4, 0));
       }
     } else {
       const __amdgpu_buffer_rsrc_t rv = cache ? rv_c : rv_n;
@@ -280,8 +311,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   };
 
-  // ---- complete the staging of tile t's keys / values (INT8: convert + store,
-  // with the per-key scales); direct copies are waited for by wait_copies()
+  // ---- complete the staging of tile t's keys / values (INT8: convert + store);
+  // direct copies are waited for by wait_copies()
   auto finish_k = [&](int t, int i) {
     bool cache;
     int key0, nvalid;
@@ -297,14 +328,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
       }
-      // the tile's K and V scales travel with its keys (the value scales are
-      // needed by the softmax, which may run before the values are resident)
-      float* sc = reinterpret_cast<float*>(Ks + C::KT_BYTES);
-      for (int j = tid; j < 2 * BC; j += C::NT) {
-        const int kidx = j % BC;
-        const float* src = j < BC ? a.ks : a.vs;
-        sc[j] = kidx < nvalid ? src[(int64_t)h * a.pitch_c + key0 + kidx] : 0.f;
-      }
+      // the tile's key scales travel with its keys
+      if (tid < BC) reinterpret_cast<float*>(Ks + C::KT_BYTES)[tid] = sks;
     }
   };
   auto finish_v = [&](int t, int i) {
@@ -317,7 +342,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       for (int j = 0; j < C::NV8; ++j) {
         const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
         u32x4 lo, hi;
-        i8x16_to_bf16(stv[j], lo, hi);
+        i8x16_dequant_bf16(stv[j], svs[j], lo, hi);
         const int s = swz_v<BC>(d);
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
@@ -411,7 +436,6 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   auto raise_ref = [&](int qb, float mt) {
     const float mn = fmaxf(m_ref[qb], mt);
     const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
-    l_add[qb] *= alpha;
     lacc[qb] *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[qb][db] *= alpha;
@@ -423,12 +447,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // of the tile exceeds it by more than kTau (always on the first tile, where it
   // is -inf). Every probability is thus at most 2^kTau, and raises are rare
   // after the first tile. Each lane tests the maximum of its own logits; a raise
-  // takes the exact tile max over the query's four lanes. INT8 values: the row
-  // sum takes p_j, the MFMA operand p_j * v_scale_j (scales stored beside the
-  // tile's keys in K buffer i).
-  auto probs = [&](int i, const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
-    constexpr bool SCALED = decltype(scaled_tag)::value;
-    const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES) + BC;
+  // takes the exact tile max over the query's four lanes.
+  auto probs = [&](const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -445,17 +465,6 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) p[4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
-        if constexpr (SCALED) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) l_add[qb] += p[r];
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 32 * g + 8 * G + 4);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[r] *= v0[r];
-            p[4 + r] *= v1[r];
-          }
-        }
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
@@ -464,8 +473,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   };
 
-  // O^T += V^T P^T from V buffer i; unscaled tiles also add their row sums with
-  // an all-ones A operand. The V fragments of key group g+1 are requested into
+  // O^T += V^T P^T from V buffer i, plus the row sums by an all-ones A operand. The V fragments of key group g+1 are requested into
   // the registers of group g as each is consumed, so their LDS latency hides
   // behind the remaining MFMAs (the scheduling barriers keep that order).
   const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
@@ -478,14 +486,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     for (int db = 0; db < D / 16; ++db) vf[db] = vread(i, 0, db);
   };
   // vf: key group 0's fragments, already requested
-  auto values_from = [&](int i, const bf16x8 (&pf)[QB][BC / 32], bf16x8 (&vf)[D / 16], auto scaled_tag) {
-    constexpr bool SCALED = decltype(scaled_tag)::value;
+  auto values_from = [&](int i, const bf16x8 (&pf)[QB][BC / 32], bf16x8 (&vf)[D / 16]) {
 #pragma unroll
     for (int g = 0; g < BC / 32; ++g) {
-      if constexpr (!SCALED) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][g], lacc[qb], 0, 0, 0);
-      }
+      for (int qb = 0; qb < QB; ++qb) lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][g], lacc[qb], 0, 0, 0);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
 #pragma unroll
@@ -497,12 +502,12 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   };
   // then() runs right after the first group's requests (the caller's next reads)
-  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto scaled_tag, auto&& then) {
+  auto values = [&](int i, const bf16x8 (&pf)[QB][BC / 32], auto&& then) {
     bf16x8 vf[D / 16];
     read_v0(i, vf);
     then();
     __builtin_amdgcn_sched_barrier(0);
-    values_from(i, pf, vf, scaled_tag);
+    values_from(i, pf, vf);
   };
   auto no_reads = []() {};
 
@@ -553,9 +558,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         bf16x8 k0[KH];   // first K fragments of tile t, landing during the value MFMAs
         if constexpr (VPF) {
           read_k0(t & 1, k0);
-          if (t >= 1) values_from(vb(t - 1), pf, vf, scaled_tag);
+          if (t >= 1) values_from(vb(t - 1), pf, vf);
         } else {
-          if (t >= 1) values(vb(t - 1), pf, scaled_tag, [&]() { read_k0(t & 1, k0); });
+          if (t >= 1) values(vb(t - 1), pf, [&]() { read_k0(t & 1, k0); });
           else read_k0(t & 1, k0);
         }
         logits_from(t & 1, k0, sacc, scaled_tag);
@@ -563,13 +568,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         __syncthreads();
         // H2(t)
         if (grp == 1) issue(t + 2);
-        probs(t & 1, sacc, pf, scaled_tag);
+        probs(sacc, pf);
         if constexpr (VPF) read_v0(vb(t), vf);
         if (grp == 0) complete(t + 1);
         __syncthreads();
       }
-      if constexpr (VPF) values_from(vb(n - 1), pf, vf, scaled_tag);
-      else values(vb(n - 1), pf, scaled_tag, no_reads);
+      if constexpr (VPF) values_from(vb(n - 1), pf, vf);
+      else values(vb(n - 1), pf, no_reads);
       __syncthreads();
       if (grp == 0) __syncthreads();   // group A's idle last slot
     } else {
@@ -589,8 +594,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         f32x4 s[QB][NKB];
         logits(i, s, scaled_tag);
         bf16x8 pf[QB][BC / 32];
-        probs(i, s, pf, scaled_tag);
-        values(i, pf, scaled_tag, no_reads);
+        probs(s, pf);
+        values(i, pf, no_reads);
         if (more) {
           finish_k(t0 + j + 1, i ^ 1);
           finish_v(t0 + j + 1, i ^ 1);
@@ -618,8 +623,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     logits(0, s, scaled_tag);
     mask_tail(s, nvalid);
     bf16x8 pf[QB][BC / 32];
-    probs(0, s, pf, scaled_tag);
-    values(0, pf, scaled_tag, no_reads);
+    probs(s, pf);
+    values(0, pf, no_reads);
     __syncthreads();
   };
 
@@ -643,7 +648,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // ---- epilogue
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = lacc[qb][0] + xadd32(xadd16(l_add[qb]));
+    const float l = lacc[qb][0];
     const float inv = 1.0f / l;
     const int row = qt * C::BR + (wave * QB + qb) * 16 + i16;
     if (row >= a.n_q) continue;

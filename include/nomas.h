@@ -196,6 +196,51 @@ int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const 
                                 float softmax_scale, int32_t n_splits,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One segment of a multi-segment call: n_video video rows (frames t0, t0+1, ...,
+ * tokens_per_frame rows each, in (frame, row, col) order) followed by n_text
+ * text rows.
+ */
+typedef struct {
+  int32_t n_video;
+  int32_t n_text;
+  int32_t t0;
+} nomas_segment;
+
+/* Workspace bytes nomas_block_causal_attention needs (0 on invalid arguments). */
+size_t nomas_block_causal_attention_workspace_bytes(const nomas_segment* segs, int32_t n_segments,
+                                                    int32_t tokens_per_frame, int32_t n_heads,
+                                                    int32_t head_dim);
+
+/*
+ * Block-causal attention over several segments at once (the whole-sequence
+ * form of the segment-wise causal joint attention, as in training): the joint
+ * sequence is the segments' rows in order, [video_0; text_0; video_1; text_1;
+ * ...], and q, k, v hold all of them.
+ * A key row j is visible to a query row i iff j is in i's segment, or j is a
+ * video row of an earlier segment whose frame is >= t0(seg(i)) - window_frames
+ * (window_frames < 0: every earlier video row). Text rows of earlier segments
+ * are never visible.
+ * out[r, h, :] = sum_j softmax_j(softmax_scale * <q[r,h,:], k[j,h,:]>) v[j,h,:]
+ * over the visible j; lse[h*n_rows + r] its log-sum-exp (if lse != NULL).
+ * Pages: "segment-wise causal joint attention", madebyagents.com "Hy-Nomas";
+ * the cached call nomas_segment_attention reproduces segment s's rows of this
+ * with the cache holding the window of earlier frames.
+ * segs: (host) n_segments in [1, 64] entries; each n_video a multiple of
+ * tokens_per_frame, n_text >= 0, n_video + n_text >= 1, t0 >= 0.
+ * q, k, v: (device) bf16 [n_rows][ld_qkv]; out: (device) bf16 [n_rows][ld_out];
+ * lse: (device) float32 [n_heads][n_rows] or NULL. head_dim 64 or 128.
+ * workspace: (device), 256-byte aligned, >= the bytes above. Arithmetic as in
+ * nomas_segment_attention (bf16 MFMA products, float32 accumulation and softmax;
+ * bitwise reproducible run to run).
+ */
+int32_t nomas_block_causal_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
+                                     const nomas_segment* segs, int32_t n_segments,
+                                     int32_t tokens_per_frame, int32_t window_frames, int32_t n_heads,
+                                     int32_t head_dim, uint16_t* out, int64_t ld_out, float* lse,
+                                     float softmax_scale, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

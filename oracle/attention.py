@@ -125,7 +125,7 @@ def split_attention(q, k, v, n_splits, scale):
     return out, lse
 
 
-def block_causal_full(segments, window_frames=None, scale=None):
+def block_causal_full(segments, window_frames=None, scale=None, rows=None, return_lse=False):
     """Whole session as one sequence under the block-causal visibility mask.
 
     ``segments`` is a list, in session order, of dicts with
@@ -136,27 +136,28 @@ def block_causal_full(segments, window_frames=None, scale=None):
       t0, n_frames, tpf : first latent frame, frames, tokens per frame
     Key j is visible to query i iff seg(j) == seg(i), or seg(j) < seg(i), j is
     a video token and frame(j) >= t0(seg(i)) - window_frames.
-    Returns the list of per-segment outputs [rows, H, D].
+    ``rows``: optional per-segment arrays of the query rows to compute (None:
+    all). Returns the list of per-segment outputs [rows, H, D], and with
+    ``return_lse`` also the list of per-segment log-sum-exps [H, rows].
     """
-    rows = []           # (segment id, is_video, frame)
+    key_rows = []       # (segment id, is_video, frame)
     for sid, sg in enumerate(segments):
         nv = sg["n_frames"] * sg["tpf"]
         nt = sg["q"].shape[0] - nv
         for i in range(nv):
-            rows.append((sid, True, sg["t0"] + i // sg["tpf"]))
+            key_rows.append((sid, True, sg["t0"] + i // sg["tpf"]))
         for i in range(nt):
-            rows.append((sid, False, -1))
-    seg_id = np.array([r[0] for r in rows])
-    is_vid = np.array([r[1] for r in rows])
-    frame = np.array([r[2] for r in rows])
+            key_rows.append((sid, False, -1))
+    seg_id = np.array([r[0] for r in key_rows])
+    is_vid = np.array([r[1] for r in key_rows])
+    frame = np.array([r[2] for r in key_rows])
     H, D = segments[0]["q"].shape[1:]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    outs = []
-    start = 0
+    outs, lses = [], []
     for sid, sg in enumerate(segments):
-        n_rows = sg["q"].shape[0]
-        qi = np.asarray(sg["q"], np.float64)
+        sel = np.arange(sg["q"].shape[0]) if rows is None or rows[sid] is None else np.asarray(rows[sid])
+        qi = np.asarray(sg["q"], np.float64)[sel]
         # keys as seen by this segment: own rows raw, earlier video rows as cached
         ks, vs = [], []
         for tid, tg in enumerate(segments):
@@ -173,15 +174,16 @@ def block_causal_full(segments, window_frames=None, scale=None):
         v = np.concatenate(vs, 0)
         lower = -np.inf if window_frames is None else sg["t0"] - window_frames
         visible = (seg_id == sid) | ((seg_id < sid) & is_vid & (frame >= lower))
-        out = np.empty((n_rows, H, D))
+        out = np.empty((len(sel), H, D))
+        lse = np.empty((H, len(sel)))
         for h in range(H):
             s = scale * (qi[:, h, :] @ k[:, h, :].T)
             s = np.where(visible[None, :], s, -np.inf)
-            p, _ = _softmax_rows(s)
+            p, lse[h] = _softmax_rows(s)
             out[:, h, :] = p @ v[:, h, :]
         outs.append(out)
-        start += n_rows
-    return outs
+        lses.append(lse)
+    return (outs, lses) if return_lse else outs
 
 
 def brute_force_attention(q, k, v, scale):

@@ -82,6 +82,21 @@ struct AttnArgs {
   int per_xcd;
 };
 
+// Segments of a multi-segment call (the joint sequence [video_0; text_0;
+// video_1; ...]): segment s owns rows [row0[s], row0[s+1]), its first nv[s] rows
+// being video of frames t0[s], t0[s]+1, ... (tpf rows each); its query tiles are
+// the global tiles [qtile0[s], qtile0[s+1]). window < 0: no window.
+constexpr int kMaxSegments = 64;
+struct SegTable {
+  int n_seg;
+  int tpf;
+  int window;
+  int row0[kMaxSegments + 1];
+  int nv[kMaxSegments];
+  int t0[kMaxSegments];
+  int qtile0[kMaxSegments + 1];
+};
+
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
   return D == 128 ? ((row & 3) | (((row >> 3) & 3) << 2)) : ((row & 3) | (((row >> 3) & 1) << 2));
@@ -174,8 +189,10 @@ struct AttnCfg {
   static_assert((BC * D / 16) % NT == 0 && NK8 >= 1 && NV8 >= 1, "int8 tile must split evenly over threads");
 };
 
-template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF>
-__global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a) {
+// MS: multi-segment call (no cache; keys are rows of the joint sequence, see
+// SegTable); otherwise a segment against the cache.
+template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF, bool MS>
+__global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a, const SegTable st) {
   using C = AttnCfg<D, QB, NW, BC, I8, PIPE, VPF>;
   constexpr int NKB = C::NKB, KK = C::KK;
   constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
@@ -199,15 +216,24 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 4, i16 = lane & 15;
 
+  // the block's query rows [q_row0, q_row0 + BR) clipped to q_end; MS: the
+  // segment the query tile belongs to
+  int seg = 0, q_row0 = qt * C::BR, q_end = a.n_q;
+  if constexpr (MS) {
+    while (seg + 1 < st.n_seg && st.qtile0[seg + 1] <= qt) ++seg;
+    q_row0 = st.row0[seg] + (qt - st.qtile0[seg]) * C::BR;
+    q_end = st.row0[seg + 1];
+  }
+
   // ---- Q fragments (B operand of S^T = K Q^T): lane -> query i16, dims 32kk+8G..+8
   bf16x8 qf[QB][KK];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qt * C::BR + (wave * QB + qb) * 16 + i16;
+    const int row = q_row0 + (wave * QB + qb) * 16 + i16;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
-      if (row < a.n_q) v = *reinterpret_cast<const u32x4*>(a.q + (int64_t)row * a.ld_qkv + (int64_t)h * D + 32 * kk + 8 * G);
+      if (row < q_end) v = *reinterpret_cast<const u32x4*>(a.q + (int64_t)row * a.ld_qkv + (int64_t)h * D + 32 * kk + 8 * G);
       qf[qb][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -250,8 +276,16 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   float sks = 0.f;
   f32x4 svs[I8 ? C::NV8 : 1][4];
 
+  // MS: the key range [kbase, kend) of the joint sequence being visited
+  int kbase = 0, kend = 0;
   // tile t -> (is cache tile, first key inside its part, valid keys)
   auto tile_info = [&](int t, bool& cache, int& key0, int& nvalid) {
+    if constexpr (MS) {
+      cache = false;
+      key0 = kbase + t * BC;
+      nvalid = min(BC, kend - key0);
+      return;
+    }
     cache = t < a.tiles_c;
     key0 = (cache ? t : t - a.tiles_c) * BC;
     nvalid = min(BC, (cache ? a.n_cached : a.n_cur) - key0);
@@ -630,28 +664,47 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 
   using T_ = std::true_type;
   using F_ = std::false_type;
-  // this split's tiles: full cache tiles, full current tiles, then the partial
-  // tail of each part (key order does not matter to attention)
-  const int full_c = a.n_cached / BC, full_n = a.n_cur / BC;
-  const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
-  const int n_lo = max(t_begin, a.tiles_c), n_hi = min(t_end, a.tiles_c + full_n);
-  if (I8) run_full(c_lo, c_hi - c_lo, T_{});
-  else run_full(c_lo, c_hi - c_lo, F_{});
-  run_full(n_lo, max(0, n_hi - n_lo), F_{});
-  if (full_c < a.tiles_c && t_begin <= full_c && full_c < t_end) {
-    if (I8) run_partial(full_c, T_{});
-    else run_partial(full_c, F_{});
+  if constexpr (MS) {
+    // block-causal visibility of a query in segment seg: every row of seg, and
+    // the video rows of each earlier segment whose frame is >= t0[seg] - window
+    for (int r = 0; r <= seg; ++r) {
+      kbase = st.row0[r];
+      kend = st.row0[r + 1];
+      if (r < seg) {
+        const int nf = st.nv[r] / st.tpf;
+        const int fmin = st.window < 0 ? st.t0[r] : max(st.t0[r], st.t0[seg] - st.window);
+        if (fmin >= st.t0[r] + nf) continue;
+        kbase += (fmin - st.t0[r]) * st.tpf;
+        kend = st.row0[r] + st.nv[r];
+      }
+      const int nfull = (kend - kbase) / BC;
+      run_full(0, nfull, F_{});
+      if (nfull * BC < kend - kbase) run_partial(nfull, F_{});
+    }
+  } else {
+    // this split's tiles: full cache tiles, full current tiles, then the partial
+    // tail of each part (key order does not matter to attention)
+    const int full_c = a.n_cached / BC, full_n = a.n_cur / BC;
+    const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
+    const int n_lo = max(t_begin, a.tiles_c), n_hi = min(t_end, a.tiles_c + full_n);
+    if (I8) run_full(c_lo, c_hi - c_lo, T_{});
+    else run_full(c_lo, c_hi - c_lo, F_{});
+    run_full(n_lo, max(0, n_hi - n_lo), F_{});
+    if (full_c < a.tiles_c && t_begin <= full_c && full_c < t_end) {
+      if (I8) run_partial(full_c, T_{});
+      else run_partial(full_c, F_{});
+    }
+    const int pn = a.tiles_c + full_n;
+    if (pn < a.tiles_total && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
   }
-  const int pn = a.tiles_c + full_n;
-  if (pn < a.tiles_total && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
 
   // ---- epilogue
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = lacc[qb][0];
     const float inv = 1.0f / l;
-    const int row = qt * C::BR + (wave * QB + qb) * 16 + i16;
-    if (row >= a.n_q) continue;
+    const int row = q_row0 + (wave * QB + qb) * 16 + i16;
+    if (row >= q_end) continue;
     const float lse = (m_ref[qb] + log2f(l)) * kLn2;
     if (!a.part_o) {
       uint16_t* dst = a.out + (int64_t)row * a.ld_out + (int64_t)h * D + 4 * G;
@@ -797,11 +850,12 @@ static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, i
   return true;
 }
 
-template <int D, bool I8>
-static void launch_attn(const AttnArgs& a, hipStream_t st) {
+template <int D, bool I8, bool MS = false>
+static void launch_attn(const AttnArgs& a, hipStream_t st, const SegTable& seg) {
   const dim3 grid((unsigned)(8 * a.per_xcd));
   using S = Shape<D, I8>;
-  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE, S::VPF>), grid, dim3(S::NW * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE, S::VPF, MS>), grid, dim3(S::NW * 64), 0, st, a,
+                     seg);
 }
 
 }  // namespace nomas
@@ -888,12 +942,13 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
   a.n_blocks = p.n_qtiles * H * p.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
   const bool i8 = c->kv_dtype == NOMAS_KV_INT8;
+  const SegTable none{};
   if (D == 128) {
-    if (i8) launch_attn<128, true>(a, st);
-    else launch_attn<128, false>(a, st);
+    if (i8) launch_attn<128, true>(a, st, none);
+    else launch_attn<128, false>(a, st, none);
   } else {
-    if (i8) launch_attn<64, true>(a, st);
-    else launch_attn<64, false>(a, st);
+    if (i8) launch_attn<64, true>(a, st, none);
+    else launch_attn<64, false>(a, st, none);
   }
   if (int32_t e = check_launch("segment_attention")) return e;
   if (p.splits > 1) {
@@ -907,4 +962,121 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
     if (int32_t e = check_launch("segment_attention (merge)")) return e;
   }
   return ok();
+}
+
+// ---------------------------------------------------------------- multi-segment calls
+namespace nomas {
+
+struct SegPlan {
+  SegTable t;
+  int n_rows, pitch, n_qtiles;
+  size_t bytes;
+};
+
+static int32_t make_seg_plan(const nomas_segment* segs, int32_t n_segments, int32_t tpf, int32_t window, int H, int D,
+                             SegPlan& p, const char* who) {
+  if (!segs || n_segments < 1 || n_segments > kMaxSegments)
+    return fail(NOMAS_E_INVALID, "%s: need 1 <= n_segments <= %d and a segment array", who, kMaxSegments);
+  if (tpf < 1) return fail(NOMAS_E_INVALID, "%s: tokens_per_frame must be >= 1", who);
+  if (H < 1 || (D != 64 && D != 128)) return fail(NOMAS_E_UNSUPPORTED, "%s: head_dim must be 64 or 128, n_heads >= 1", who);
+  p.t = SegTable{};
+  p.t.n_seg = n_segments;
+  p.t.tpf = tpf;
+  p.t.window = window < 0 ? -1 : window;
+  const int br = block_queries(D);
+  int64_t rows = 0, tiles = 0;
+  for (int s = 0; s < n_segments; ++s) {
+    const nomas_segment& g = segs[s];
+    if (g.n_video < 0 || g.n_text < 0 || (int64_t)g.n_video + g.n_text < 1 || g.n_video % tpf || g.t0 < 0)
+      return fail(NOMAS_E_INVALID,
+                  "%s: segment %d needs n_video >= 0 (a multiple of tokens_per_frame), n_text >= 0, "
+                  "n_video + n_text >= 1, t0 >= 0", who, s);
+    p.t.row0[s] = (int)rows;
+    p.t.nv[s] = g.n_video;
+    p.t.t0[s] = g.t0;
+    p.t.qtile0[s] = (int)tiles;
+    rows += (int64_t)g.n_video + g.n_text;
+    tiles += ((int64_t)g.n_video + g.n_text + br - 1) / br;
+    if (rows > (1 << 26)) return fail(NOMAS_E_INVALID, "%s: more than 2^26 rows", who);
+  }
+  p.t.row0[n_segments] = (int)rows;
+  p.t.qtile0[n_segments] = (int)tiles;
+  p.n_rows = (int)rows;
+  p.n_qtiles = (int)tiles;
+  p.pitch = (int)round_up(rows, kTokenAlign);
+  p.bytes = round_up((int64_t)H * D * p.pitch * 2, 256);
+  return NOMAS_OK;
+}
+
+}  // namespace nomas
+
+extern "C" size_t nomas_block_causal_attention_workspace_bytes(const nomas_segment* segs, int32_t n_segments,
+                                                               int32_t tokens_per_frame, int32_t n_heads,
+                                                               int32_t head_dim) {
+  SegPlan p;
+  if (make_seg_plan(segs, n_segments, tokens_per_frame, -1, n_heads, head_dim, p, "block_causal_attention")) return 0;
+  return p.bytes;
+}
+
+extern "C" int32_t nomas_block_causal_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld_qkv,
+                                                const nomas_segment* segs, int32_t n_segments,
+                                                int32_t tokens_per_frame, int32_t window_frames, int32_t n_heads,
+                                                int32_t head_dim, uint16_t* out, int64_t ld_out, float* lse,
+                                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  const char* who = "block_causal_attention";
+  const int H = n_heads, D = head_dim;
+  SegPlan p;
+  if (int32_t e = make_seg_plan(segs, n_segments, tokens_per_frame, window_frames, H, D, p, who)) return e;
+  if (!q || !k || !v || !out) return fail(NOMAS_E_INVALID, "%s: q, k, v, out must be non-NULL", who);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(NOMAS_E_INVALID, "%s: q, k, v, out must be 16-byte aligned", who);
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(NOMAS_E_INVALID, "%s: lse must be 4-byte aligned", who);
+  if (ld_qkv < (int64_t)H * D || ld_qkv % 8 || ld_out < (int64_t)H * D || ld_out % 8)
+    return fail(NOMAS_E_INVALID, "%s: ld_qkv and ld_out must be >= n_heads*head_dim and multiples of 8", who);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(NOMAS_E_INVALID, "%s: softmax_scale must be finite and > 0", who);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(NOMAS_E_WORKSPACE, "%s: workspace must be non-NULL and 256-byte aligned", who);
+  if (workspace_bytes < p.bytes)
+    return fail(NOMAS_E_WORKSPACE, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, p.bytes);
+
+  const hipStream_t st = as_stream(stream);
+  uint16_t* vt = static_cast<uint16_t*>(workspace);
+  {
+    const dim3 grid((unsigned)(p.pitch / 64), (unsigned)H);
+    if (D == 128) hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, v, ld_qkv, p.n_rows, vt, p.pitch);
+    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, st, v, ld_qkv, p.n_rows, vt, p.pitch);
+    if (int32_t e = check_launch("block_causal_attention (v transpose)")) return e;
+  }
+  AttnArgs a{};
+  a.q = q;
+  a.kcur = k;
+  a.ld_qkv = ld_qkv;
+  a.vtcur = vt;
+  a.pitch_cur = p.pitch;
+  a.kc = k;          // no cache: the descriptors over it are never read
+  a.vc = v;
+  a.ks = nullptr;
+  a.vs = nullptr;
+  a.pitch_c = 0;
+  a.n_cached = 0;
+  a.n_cur = p.n_rows;
+  a.n_q = p.n_rows;
+  a.H = H;
+  a.c2 = softmax_scale * kLog2e;
+  a.out = out;
+  a.ld_out = ld_out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  a.n_splits = 1;
+  a.tiles_c = 0;
+  a.tiles_total = 0;
+  a.n_qtiles = p.n_qtiles;
+  a.n_blocks = p.n_qtiles * H;
+  a.per_xcd = (a.n_blocks + 7) / 8;
+  if (D == 128) launch_attn<128, false, true>(a, st, p.t);
+  else launch_attn<64, false, true>(a, st, p.t);
+  return check_launch(who);
 }

@@ -43,6 +43,11 @@ class KVCacheDesc(ctypes.Structure):
     ]
 
 
+class Segment(ctypes.Structure):
+    """Mirror of ``nomas_segment`` in include/nomas.h."""
+    _fields_ = [("n_video", ctypes.c_int32), ("n_text", ctypes.c_int32), ("t0", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -56,6 +61,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     desc_p = ctypes.POINTER(KVCacheDesc)
+    seg_p = ctypes.POINTER(Segment)
     sig = {
         "nomas_version": (i32, []),
         "nomas_last_error": (ctypes.c_char_p, []),
@@ -68,6 +74,9 @@ def lib():
         "nomas_segment_attention_workspace_bytes": (sz, [i32, i32, i64, i32, i32, i32, i32]),
         "nomas_segment_attention_splits": (i32, [i32, i32, i64, i32, i32, i32, i32]),
         "nomas_segment_attention": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp, sz, vp]),
+        "nomas_block_causal_attention_workspace_bytes": (sz, [seg_p, i32, i32, i32, i32]),
+        "nomas_block_causal_attention": (i32, [vp, vp, vp, i64, seg_p, i32, i32, i32, i32, i32, vp, i64, vp, f32,
+                                               vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -225,4 +234,55 @@ def nomas_segment_attention(q, k_cur, v_cur, n_video, n_text, cache, out=None, l
     _check(lib().nomas_segment_attention(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d), op, ldo, lp, scale,
                                          n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                          _stream(stream)))
+    return out
+
+
+def _segments(segments):
+    """[(n_video, n_text, t0), ...] -> ctypes array of nomas_segment."""
+    arr = (Segment * len(segments))()
+    for i, (nv, nt, t0) in enumerate(segments):
+        arr[i] = Segment(int(nv), int(nt), int(t0))
+    return arr
+
+
+def nomas_block_causal_attention_workspace_bytes(segments, tokens_per_frame, n_heads, head_dim):
+    return lib().nomas_block_causal_attention_workspace_bytes(_segments(segments), len(segments), tokens_per_frame,
+                                                              n_heads, head_dim)
+
+
+def nomas_block_causal_attention(q, k, v, segments, tokens_per_frame, window_frames, n_heads, head_dim, out=None,
+                                 lse=None, softmax_scale=None, workspace=None, stream=None):
+    """Block-causal attention over several segments at once.
+
+    ``segments``: [(n_video, n_text, t0), ...] in sequence order; q, k, v hold
+    their rows [video_0; text_0; video_1; ...]. ``window_frames`` < 0: no window.
+    Returns ``out`` ([n_rows, H, D] bf16, allocated if not given)."""
+    H, D = n_heads, head_dim
+    segs = _segments(segments)
+    n_rows = sum(int(nv) + int(nt) for nv, nt, _ in segments)
+    qp, ld = _rows_view(q, "q", H, D)
+    kp, ldk = _rows_view(k, "k", H, D)
+    vp, ldv = _rows_view(v, "v", H, D)
+    if not (ld == ldk == ldv):
+        raise ValueError("q, k, v must share a row stride")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.shape[0] < n_rows:
+            raise ValueError(f"{name} holds fewer rows than the segments")
+    if out is None:
+        out = torch.empty((n_rows, H, D), dtype=torch.bfloat16, device=q.device)
+    op, ldo = _rows_view(out, "out", H, D)
+    if out.shape[0] < n_rows:
+        raise ValueError("out holds fewer rows than the segments")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() < H * n_rows:
+            raise ValueError("lse must be a contiguous float32 tensor of n_heads*n_rows elements")
+        lp = ctypes.c_void_p(lse.data_ptr())
+    if workspace is None:
+        nb = nomas_block_causal_attention_workspace_bytes(segments, tokens_per_frame, H, D)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().nomas_block_causal_attention(qp, kp, vp, ld, segs, len(segments), tokens_per_frame, window_frames,
+                                              H, D, op, ldo, lp, scale, ctypes.c_void_p(workspace.data_ptr()),
+                                              workspace.numel(), _stream(stream)))
     return out

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_names_match_the_c_entry_points():
     for n in ["nomas_rope3d", "nomas_segment_attention", "nomas_segment_attention_workspace_bytes",
-              "nomas_segment_attention_splits", "nomas_kvcache_bytes", "nomas_version"]:
+              "nomas_segment_attention_splits", "nomas_kvcache_bytes", "nomas_version",
+              "nomas_block_causal_attention", "nomas_block_causal_attention_workspace_bytes"]:
         assert callable(getattr(nomas, n))
     assert callable(nomas.KVCache.nomas_kvcache_append)
 
@@ -151,3 +152,32 @@ def test_workspace_and_split_planning():
     assert L.nomas_segment_attention_workspace_bytes(0, 0, 0, 16, 128, BF16, 0) == 0
     assert L.nomas_segment_attention_splits(10, 0, 0, 1, 96, BF16, 0) == -1
     assert L.nomas_segment_attention_splits(10, 0, 0, 1, 64, 7, 0) == -1
+
+
+def test_block_causal_rejects_before_launch():
+    L = nomas.lib()
+    segs = nomas._segments([(48, 16, 0), (48, 16, 2)])
+    need = L.nomas_block_causal_attention_workspace_bytes(segs, 2, 24, 2, 64)
+    assert need == 2 * 64 * 128 * 2          # V^T of 128 rows (one 128-row pitch)
+    p = ctypes.c_void_p(1 << 24)
+    ws = ctypes.c_void_p(1 << 26)
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, ld=128, segs=segs, n=2, tpf=24, win=-1, H=2, D=64, out=p, ldo=128, lse=None,
+                 scale=0.125, ws=ws, wsb=need)
+        a.update(kw)
+        return L.nomas_block_causal_attention(a["q"], a["k"], a["v"], a["ld"], a["segs"], a["n"], a["tpf"], a["win"],
+                                              a["H"], a["D"], a["out"], a["ldo"], a["lse"], a["scale"], a["ws"],
+                                              a["wsb"], None)
+    assert call(n=0) == nomas.NOMAS_E_INVALID
+    assert call(n=65) == nomas.NOMAS_E_INVALID
+    assert call(tpf=25) == nomas.NOMAS_E_INVALID              # 48 video rows not a multiple
+    assert call(segs=nomas._segments([(0, 0, 0), (48, 16, 2)])) == nomas.NOMAS_E_INVALID
+    assert call(segs=nomas._segments([(48, 16, -1), (48, 16, 2)])) == nomas.NOMAS_E_INVALID
+    assert call(D=96) == nomas.NOMAS_E_UNSUPPORTED
+    assert call(q=None) == nomas.NOMAS_E_INVALID
+    assert call(ld=64) == nomas.NOMAS_E_INVALID
+    assert call(scale=0.0) == nomas.NOMAS_E_INVALID
+    assert call(wsb=need - 1) == nomas.NOMAS_E_WORKSPACE
+    assert call(ws=None) == nomas.NOMAS_E_WORKSPACE
+    assert b"workspace" in L.nomas_last_error()

@@ -144,24 +144,36 @@ def _session(int8, window, n_segments=4, F=2, gh=4, gw=6, T=16, H=2, D=64):
         past = ring.retained()
         k_past = np.concatenate([p[0] for _, p in past], 0) if past else None
         v_past = np.concatenate([p[1] for _, p in past], 0) if past else None
-        out, _ = attention.segment_attention(q, k, v, k_past, v_past, 1 / math.sqrt(D))
-        cached_out.append(out)
+        out, lse = attention.segment_attention(q, k, v, k_past, v_past, 1 / math.sqrt(D))
+        cached_out.append((out, lse))
         ring.append([(kp[f * tpf:(f + 1) * tpf], vp[f * tpf:(f + 1) * tpf]) for f in range(F)])
         segs.append(dict(q=q, k=k, v=v, k_past=kp, v_past=vp, t0=t0, n_frames=F, tpf=tpf))
-    full = attention.block_causal_full(segs, window_frames=window)
-    return cached_out, full
+    full, full_lse = attention.block_causal_full(segs, window_frames=window, return_lse=True)
+    return cached_out, (full, full_lse), segs
 
 
 @pytest.mark.parametrize("int8", [False, True])
 @pytest.mark.parametrize("window", [None, 4, 3])
 def test_cached_equals_full_block_causal(int8, window):   # A5
-    cached, full = _session(int8, window)
-    for a, b in zip(cached, full):
+    cached, (full, full_lse), _ = _session(int8, window)
+    for (a, la), b, lb in zip(cached, full, full_lse):
         assert np.max(np.abs(a - b)) < 1e-12
+        assert np.max(np.abs(la - lb)) < 1e-12
+
+
+def test_block_causal_row_subset():
+    # computing selected query rows only gives those rows of the full result (to
+    # BLAS blocking order)
+    _, (full, full_lse), segs = _session(False, 3)
+    rows = [np.array([0, 7, 63]), None, np.array([5]), np.array([63, 1, 48])]
+    sub, sub_lse = attention.block_causal_full(segs, window_frames=3, rows=rows, return_lse=True)
+    for r, a, la, b, lb in zip(rows, full, full_lse, sub, sub_lse):
+        r = np.arange(a.shape[0]) if r is None else r
+        assert np.max(np.abs(a[r] - b)) < 1e-14 and np.max(np.abs(la[:, r] - lb)) < 1e-13
 
 
 def test_window_changes_result():
     # guard against a mask that ignores the window: W=3 must differ from W=None
-    a, _ = _session(False, None)
-    b, _ = _session(False, 3)
-    assert np.max(np.abs(a[-1] - b[-1])) > 1e-3
+    a, _, _ = _session(False, None)
+    b, _, _ = _session(False, 3)
+    assert np.max(np.abs(a[-1][0] - b[-1][0])) > 1e-3

@@ -11,6 +11,8 @@ tokens, 8-frame segment = 7,680 video tokens + 256 text tokens):
 Also reported (outside the timed steps):
   * the attention launch alone (HIP events on the launch stream) against the
     bf16 MFMA peak -> ``roofline``;
+  * one multi-segment block-causal call at a training shape (4 segments x 7,936
+    rows, 18-frame window) -> ``block_causal_tflops``;
   * the full denoise sweep: 54 layers x 8 steps x 3 turns of RoPE + attention
     against per-layer INT8 18-frame windows, with the 54 appends after step 8
     of each turn -> ``denoise_ms_per_step`` (median over the 24 steps);
@@ -168,6 +170,41 @@ def denoise_bench(n_turns=3):
                 + 2 * wl.n_video * H * 4)
 
 
+def block_causal_bench(reps=20):
+    """Multi-segment call at a training shape: 4 segments of 8 frames on the
+    24x40 grid + 256 text rows each (31,744 rows), 16x128 heads, 18-frame window."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    H, D, tpf, F, T, W = 16, 128, 960, 8, 256, 18
+    segments = [(F * tpf, T, F * s) for s in range(4)]
+    n = sum(nv + nt for nv, nt, _ in segments)
+    q, k, v = (dev_bf16(synth.normal_bf16((n, H, D), 77, 0, 0, t)) for t in range(3))
+    out = torch.empty_like(q)
+    nb = nomas.nomas_block_causal_attention_workspace_bytes(segments, tpf, H, D)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    # visible keys per query segment: its own rows + earlier video frames >= t0 - W
+    flop = 0
+    for i, (nv, nt, t0) in enumerate(segments):
+        keys = nv + nt + sum(tpf * sum(1 for f in range(t0p, t0p + nvp // tpf) if f >= t0 - W)
+                             for nvp, _, t0p in segments[:i])
+        flop += 4 * (nv + nt) * keys * D * H
+    call = lambda: nomas.nomas_block_causal_attention(q, k, v, segments, tpf, W, H, D, out=out, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    log(f"[bench] block-causal 4-segment call: {ms:.3f} ms, {flop / ms / 1e9:.1f} TFLOP/s")
+    return dict(block_causal_ms=round(ms, 4), block_causal_tflops=round(flop / ms / 1e9, 1),
+                block_causal_flop=flop)
+
+
 def cpu_baseline(rows_per_head):
     """The fp64 oracle (as it stands) on a bounded sample of the layer workload."""
     import numpy as np
@@ -234,6 +271,7 @@ def main():
         extra.update(denoise_ms_per_step=round(d["denoise_ms_per_step"], 3),
                      denoise_attention_tflops=round(d["denoise_tflops"], 1),
                      denoise_append_ms_per_turn=round(d["denoise_append_ms_per_turn"], 3))
+    extra.update(block_causal_bench())
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
     line = {
         "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",

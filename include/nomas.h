@@ -197,6 +197,56 @@ int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-sparse segment attention. After two dense denoising steps the pages keep
+ * 25 % of the candidate video blocks ("Hy-Nomas auf einer RTX 4090",
+ * inferencekey.com, "Das Single-GPU-Preset", citing the tech report's 6.2); they
+ * give no block size or selection rule. Reading: candidates are the cached video
+ * keys in blocks of NOMAS_SPARSE_KEY_BLOCK consecutive cache rows (the last one
+ * may be shorter); each block of NOMAS_SPARSE_QUERY_BLOCK consecutive query rows
+ * of a head keeps its own list of candidates; the current segment's rows are
+ * always attended.
+ * block_list layout: int32 [n_heads][ceil(n_q / NOMAS_SPARSE_QUERY_BLOCK)][n_select],
+ * each list ascending, entries unique in [0, candidates).
+ */
+#define NOMAS_SPARSE_KEY_BLOCK 128
+#define NOMAS_SPARSE_QUERY_BLOCK 256
+
+/* Candidate blocks of n_cached cache rows: ceil(n_cached / 128); -1 if n_cached < 0. */
+int32_t nomas_sparse_candidates(int64_t n_cached);
+
+/* Workspace bytes of nomas_sparse_select (0 on invalid arguments). */
+size_t nomas_sparse_select_workspace_bytes(int32_t n_q, int64_t n_cached, int32_t n_heads, int32_t head_dim);
+
+/*
+ * Selection rule (a reading): per head and query block, candidate block c
+ * scores mean_q . mean_k(c) in float32 (means of the block's query rows and of
+ * the candidate's cached keys as attention sees them: bf16 values, or
+ * code*scale for INT8); the n_select highest scores are kept, equal scores
+ * going to the lower index, and written to block_list in ascending order.
+ * q: (device) bf16 [n_q][ld_q] (the queries the attention will use); c: (host)
+ * descriptor of the cache; n_select in [0, candidates], at most 8192
+ * candidates; block_list: (device) as above (untouched when n_select = 0).
+ * workspace: (device) 256-byte aligned, >= nomas_sparse_select_workspace_bytes.
+ */
+int32_t nomas_sparse_select(const uint16_t* q, int64_t ld_q, int32_t n_q, const nomas_kvcache* c,
+                            int32_t n_select, int32_t* block_list, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * nomas_segment_attention restricted, for each head and query block, to the
+ * n_select candidate blocks of block_list (plus the whole current segment).
+ * Arguments and results as nomas_segment_attention; block_list as above, read
+ * on the device (a list that breaks the stated form gives undefined results;
+ * every access still stays inside the cache buffers). Workspace: as for
+ * nomas_segment_attention_workspace_bytes with n_cached = n_select*128.
+ */
+int32_t nomas_segment_attention_sparse(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                       int64_t ld_qkv, int32_t n_video, int32_t n_text, const nomas_kvcache* c,
+                                       const int32_t* block_list, int32_t n_select, uint16_t* out,
+                                       int64_t ld_out, float* lse, float softmax_scale, int32_t n_splits,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One segment of a multi-segment call: n_video video rows (frames t0, t0+1, ...,
  * tokens_per_frame rows each, in (frame, row, col) order) followed by n_text
  * text rows.

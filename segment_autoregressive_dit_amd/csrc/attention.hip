@@ -80,7 +80,14 @@ struct AttnArgs {
   int n_qtiles;
   int n_blocks;
   int per_xcd;
+  const int32_t* blist;    // sparse: [H][nqb_sp][n_sel] candidate blocks of 128 cache rows
+  int n_sel;
+  int nqb_sp;
 };
+
+constexpr int kSpKeyBlock = NOMAS_SPARSE_KEY_BLOCK;
+constexpr int kSpQueryBlock = NOMAS_SPARSE_QUERY_BLOCK;
+enum { kModeCached = 0, kModeSegments = 1, kModeSparse = 2 };
 
 // Segments of a multi-segment call (the joint sequence [video_0; text_0;
 // video_1; ...]): segment s owns rows [row0[s], row0[s+1]), its first nv[s] rows
@@ -189,11 +196,14 @@ struct AttnCfg {
   static_assert((BC * D / 16) % NT == 0 && NK8 >= 1 && NV8 >= 1, "int8 tile must split evenly over threads");
 };
 
-// MS: multi-segment call (no cache; keys are rows of the joint sequence, see
-// SegTable); otherwise a segment against the cache.
-template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF, bool MS>
+// MODE: kModeCached (a segment against the cache), kModeSegments (multi-segment
+// call: no cache, keys are rows of the joint sequence, see SegTable) or
+// kModeSparse (against the cache blocks of a per-query-block list).
+template <int D, int QB, int NW, int BC, bool I8, bool PIPE, bool VPF, int MODE>
 __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnArgs a, const SegTable st) {
   using C = AttnCfg<D, QB, NW, BC, I8, PIPE, VPF>;
+  constexpr bool MS = MODE == kModeSegments, SP = MODE == kModeSparse;
+  static_assert(kSpKeyBlock % BC == 0 && kSpQueryBlock % C::BR == 0, "sparse blocks must be whole tiles");
   constexpr int NKB = C::NKB, KK = C::KK;
   constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
   // two K buffers, then C::NVS V^T buffers
@@ -209,8 +219,24 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const int hs = __builtin_amdgcn_readfirstlane(logical / a.n_qtiles);
   const int split = __builtin_amdgcn_readfirstlane(hs % a.n_splits);
   const int h = __builtin_amdgcn_readfirstlane(hs / a.n_splits);
-  const int t_begin = __builtin_amdgcn_readfirstlane((int)((int64_t)split * a.tiles_total / a.n_splits));
-  const int t_end = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * a.tiles_total / a.n_splits));
+
+  // cache tiles of this block: all of them, or (sparse) those of its list; the
+  // last listed block may be shorter than 128 rows
+  int tiles_c_b = a.tiles_c, full_c_b = a.n_cached / BC, tiles_total_b = a.tiles_total;
+  const int32_t* blist = nullptr;
+  constexpr int TPB = kSpKeyBlock / BC;     // tiles per candidate block
+  if constexpr (SP) {
+    blist = a.blist + ((int64_t)h * a.nqb_sp + qt * C::BR / kSpQueryBlock) * a.n_sel;
+    tiles_c_b = full_c_b = 0;
+    if (a.n_sel > 0) {
+      const int rem = max(0, min(kSpKeyBlock, a.n_cached - blist[a.n_sel - 1] * kSpKeyBlock));
+      tiles_c_b = (a.n_sel - 1) * TPB + (rem + BC - 1) / BC;
+      full_c_b = (a.n_sel - 1) * TPB + rem / BC;
+    }
+    tiles_total_b = tiles_c_b + (a.n_cur + BC - 1) / BC;
+  }
+  const int t_begin = __builtin_amdgcn_readfirstlane((int)((int64_t)split * tiles_total_b / a.n_splits));
+  const int t_end = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * tiles_total_b / a.n_splits));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -286,8 +312,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       nvalid = min(BC, kend - key0);
       return;
     }
-    cache = t < a.tiles_c;
-    key0 = (cache ? t : t - a.tiles_c) * BC;
+    cache = t < tiles_c_b;
+    if (SP && cache) key0 = blist[t / TPB] * kSpKeyBlock + (t % TPB) * BC;
+    else key0 = (cache ? t : t - tiles_c_b) * BC;
     nvalid = min(BC, (cache ? a.n_cached : a.n_cur) - key0);
   };
 
@@ -684,18 +711,18 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   } else {
     // this split's tiles: full cache tiles, full current tiles, then the partial
     // tail of each part (key order does not matter to attention)
-    const int full_c = a.n_cached / BC, full_n = a.n_cur / BC;
+    const int full_c = full_c_b, full_n = a.n_cur / BC;
     const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
-    const int n_lo = max(t_begin, a.tiles_c), n_hi = min(t_end, a.tiles_c + full_n);
+    const int n_lo = max(t_begin, tiles_c_b), n_hi = min(t_end, tiles_c_b + full_n);
     if (I8) run_full(c_lo, c_hi - c_lo, T_{});
     else run_full(c_lo, c_hi - c_lo, F_{});
     run_full(n_lo, max(0, n_hi - n_lo), F_{});
-    if (full_c < a.tiles_c && t_begin <= full_c && full_c < t_end) {
+    if (full_c < tiles_c_b && t_begin <= full_c && full_c < t_end) {
       if (I8) run_partial(full_c, T_{});
       else run_partial(full_c, F_{});
     }
-    const int pn = a.tiles_c + full_n;
-    if (pn < a.tiles_total && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
+    const int pn = tiles_c_b + full_n;
+    if (pn < tiles_total_b && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
   }
 
   // ---- epilogue
@@ -850,12 +877,12 @@ static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, i
   return true;
 }
 
-template <int D, bool I8, bool MS = false>
+template <int D, bool I8, int MODE = kModeCached>
 static void launch_attn(const AttnArgs& a, hipStream_t st, const SegTable& seg) {
   const dim3 grid((unsigned)(8 * a.per_xcd));
   using S = Shape<D, I8>;
-  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE, S::VPF, MS>), grid, dim3(S::NW * 64), 0, st, a,
-                     seg);
+  hipLaunchKernelGGL((attn_kernel<D, S::QB, S::NW, S::BC, I8, S::PIPE, S::VPF, MODE>), grid, dim3(S::NW * 64), 0, st,
+                     a, seg);
 }
 
 }  // namespace nomas
@@ -878,10 +905,12 @@ extern "C" int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_tex
   return p.splits;
 }
 
-extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
-                                           int64_t ld_qkv, int32_t n_video, int32_t n_text, const nomas_kvcache* c,
-                                           uint16_t* out, int64_t ld_out, float* lse, float softmax_scale,
-                                           int32_t n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+// the cached call, dense (sparse = false) or restricted to the block lists
+static int32_t segment_attention_impl(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur, int64_t ld_qkv,
+                                      int32_t n_video, int32_t n_text, const nomas_kvcache* c, bool sparse,
+                                      const int32_t* block_list, int32_t n_select, uint16_t* out, int64_t ld_out,
+                                      float* lse, float softmax_scale, int32_t n_splits, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   if (int32_t e = validate_cache(c, "segment_attention")) return e;
   const int H = c->n_heads, D = c->head_dim;
   if (!q || !k_cur || !v_cur || !out) return fail(NOMAS_E_INVALID, "segment_attention: q, k_cur, v_cur, out must be non-NULL");
@@ -896,8 +925,17 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
     return fail(NOMAS_E_INVALID, "segment_attention: softmax_scale must be finite and > 0");
   if (n_splits < 0) return fail(NOMAS_E_INVALID, "segment_attention: n_splits must be >= 0");
   const int64_t n_cached = nomas_kvcache_valid_frames(c) * c->tokens_per_frame;
+  const int64_t n_cand = (n_cached + kSpKeyBlock - 1) / kSpKeyBlock;
+  if (sparse) {
+    if (n_select < 0 || n_select > n_cand)
+      return fail(NOMAS_E_INVALID, "segment_attention_sparse: n_select %d outside [0, %lld] (candidate blocks)", n_select,
+                  (long long)n_cand);
+    if (n_select > 0 && (!block_list || (reinterpret_cast<uintptr_t>(block_list) & 3)))
+      return fail(NOMAS_E_INVALID, "segment_attention_sparse: block_list must be non-NULL and 4-byte aligned");
+  }
+  // splits and workspace are planned for the listed rows (an upper bound)
   Plan p;
-  if (!make_plan(n_video, n_text, n_cached, H, D, c->kv_dtype, n_splits, p))
+  if (!make_plan(n_video, n_text, sparse ? (int64_t)n_select * kSpKeyBlock : n_cached, H, D, c->kv_dtype, n_splits, p))
     return fail(NOMAS_E_INVALID, "segment_attention: sizes out of range");
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(NOMAS_E_WORKSPACE, "segment_attention: workspace must be non-NULL and 256-byte aligned");
@@ -925,7 +963,7 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
   a.ks = c->k_scale;
   a.vs = c->v_scale;
   a.pitch_c = c->token_pitch;
-  a.n_cached = p.n_cached;
+  a.n_cached = (int)n_cached;
   a.n_cur = p.n_q;
   a.n_q = p.n_q;
   a.H = H;
@@ -941,9 +979,20 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
   a.n_qtiles = p.n_qtiles;
   a.n_blocks = p.n_qtiles * H * p.splits;
   a.per_xcd = (a.n_blocks + 7) / 8;
+  a.blist = block_list;
+  a.n_sel = sparse ? n_select : 0;
+  a.nqb_sp = (p.n_q + kSpQueryBlock - 1) / kSpQueryBlock;
   const bool i8 = c->kv_dtype == NOMAS_KV_INT8;
   const SegTable none{};
-  if (D == 128) {
+  if (sparse) {
+    if (D == 128) {
+      if (i8) launch_attn<128, true, kModeSparse>(a, st, none);
+      else launch_attn<128, false, kModeSparse>(a, st, none);
+    } else {
+      if (i8) launch_attn<64, true, kModeSparse>(a, st, none);
+      else launch_attn<64, false, kModeSparse>(a, st, none);
+    }
+  } else if (D == 128) {
     if (i8) launch_attn<128, true>(a, st, none);
     else launch_attn<128, false>(a, st, none);
   } else {
@@ -962,6 +1011,24 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
     if (int32_t e = check_launch("segment_attention (merge)")) return e;
   }
   return ok();
+}
+
+extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                           int64_t ld_qkv, int32_t n_video, int32_t n_text, const nomas_kvcache* c,
+                                           uint16_t* out, int64_t ld_out, float* lse, float softmax_scale,
+                                           int32_t n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, false, nullptr, 0, out, ld_out, lse,
+                                softmax_scale, n_splits, workspace, workspace_bytes, stream);
+}
+
+extern "C" int32_t nomas_segment_attention_sparse(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                                  int64_t ld_qkv, int32_t n_video, int32_t n_text,
+                                                  const nomas_kvcache* c, const int32_t* block_list,
+                                                  int32_t n_select, uint16_t* out, int64_t ld_out, float* lse,
+                                                  float softmax_scale, int32_t n_splits, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, true, block_list, n_select, out, ld_out,
+                                lse, softmax_scale, n_splits, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- multi-segment calls
@@ -1076,7 +1143,7 @@ extern "C" int32_t nomas_block_causal_attention(const uint16_t* q, const uint16_
   a.n_qtiles = p.n_qtiles;
   a.n_blocks = p.n_qtiles * H;
   a.per_xcd = (a.n_blocks + 7) / 8;
-  if (D == 128) launch_attn<128, false, true>(a, st, p.t);
-  else launch_attn<64, false, true>(a, st, p.t);
+  if (D == 128) launch_attn<128, false, kModeSegments>(a, st, p.t);
+  else launch_attn<64, false, kModeSegments>(a, st, p.t);
   return check_launch(who);
 }

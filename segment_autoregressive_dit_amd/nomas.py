@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libnomas.so")
 
 NOMAS_OK, NOMAS_E_INVALID, NOMAS_E_UNSUPPORTED, NOMAS_E_WORKSPACE, NOMAS_E_HIP = range(5)
 NOMAS_KV_BF16, NOMAS_KV_INT8 = 0, 1
+NOMAS_SPARSE_KEY_BLOCK, NOMAS_SPARSE_QUERY_BLOCK = 128, 256
 
 
 class NomasError(RuntimeError):
@@ -75,6 +76,11 @@ def lib():
         "nomas_segment_attention_splits": (i32, [i32, i32, i64, i32, i32, i32, i32]),
         "nomas_segment_attention": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp, sz, vp]),
         "nomas_block_causal_attention_workspace_bytes": (sz, [seg_p, i32, i32, i32, i32]),
+        "nomas_sparse_candidates": (i32, [i64]),
+        "nomas_sparse_select_workspace_bytes": (sz, [i32, i64, i32, i32]),
+        "nomas_sparse_select": (i32, [vp, i64, i32, desc_p, i32, vp, vp, sz, vp]),
+        "nomas_segment_attention_sparse": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i32, vp, i64, vp, f32, i32,
+                                                 vp, sz, vp]),
         "nomas_block_causal_attention": (i32, [vp, vp, vp, i64, seg_p, i32, i32, i32, i32, i32, vp, i64, vp, f32,
                                                vp, sz, vp]),
     }
@@ -207,6 +213,45 @@ def nomas_segment_attention(q, k_cur, v_cur, n_video, n_text, cache, out=None, l
     """Attention of the current segment's rows against cache + current segment.
 
     Returns ``out`` ([n_q, H, D] bf16, allocated if not given)."""
+    return _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, None, out, lse, softmax_scale, n_splits,
+                              workspace, stream)
+
+
+def nomas_segment_attention_sparse(q, k_cur, v_cur, n_video, n_text, cache, block_list, out=None, lse=None,
+                                   softmax_scale=None, n_splits=0, workspace=None, stream=None):
+    """nomas_segment_attention restricted to the candidate blocks of ``block_list``
+    (int32 [H, ceil(n_q/256), n_select], ascending lists of 128-row cache blocks)."""
+    return _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, block_list, out, lse, softmax_scale, n_splits,
+                              workspace, stream)
+
+
+def nomas_sparse_candidates(n_cached):
+    return lib().nomas_sparse_candidates(n_cached)
+
+
+def nomas_sparse_select(q, n_q, cache, n_select, block_list=None, workspace=None, stream=None):
+    """Candidate blocks per head and 256-row query block (see nomas.h); returns
+    ``block_list`` (int32 [H, ceil(n_q/256), n_select])."""
+    d = cache.desc
+    H, D = d.n_heads, d.head_dim
+    qp, ld = _rows_view(q, "q", H, D)
+    if q.shape[0] < n_q:
+        raise ValueError("q holds fewer than n_q rows")
+    nqb = (n_q + NOMAS_SPARSE_QUERY_BLOCK - 1) // NOMAS_SPARSE_QUERY_BLOCK
+    if block_list is None:
+        block_list = torch.empty((H, nqb, max(n_select, 1)), dtype=torch.int32, device=q.device)[:, :, :n_select]
+    if block_list.dtype != torch.int32 or not block_list.is_contiguous() or block_list.numel() < H * nqb * n_select:
+        raise ValueError("block_list must be a contiguous int32 tensor of n_heads*n_qblocks*n_select elements")
+    if workspace is None:
+        nb = lib().nomas_sparse_select_workspace_bytes(n_q, cache.n_cached, H, D)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().nomas_sparse_select(qp, ld, n_q, ctypes.byref(d), n_select, ctypes.c_void_p(block_list.data_ptr()),
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return block_list
+
+
+def _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, block_list, out, lse, softmax_scale, n_splits,
+                       workspace, stream):
     d = cache.desc
     H, D = d.n_heads, d.head_dim
     n_q = n_video + n_text
@@ -228,12 +273,27 @@ def nomas_segment_attention(q, k_cur, v_cur, n_video, n_text, cache, out=None, l
         if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() < H * n_q:
             raise ValueError("lse must be a contiguous float32 tensor of n_heads*n_q elements")
         lp = ctypes.c_void_p(lse.data_ptr())
-    if workspace is None:
-        workspace = workspace_for(cache, n_video, n_text, n_splits, q.device)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    _check(lib().nomas_segment_attention(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d), op, ldo, lp, scale,
-                                         n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-                                         _stream(stream)))
+    if block_list is None:
+        if workspace is None:
+            workspace = workspace_for(cache, n_video, n_text, n_splits, q.device)
+        _check(lib().nomas_segment_attention(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d), op, ldo, lp, scale,
+                                             n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                             _stream(stream)))
+        return out
+    nqb = (n_q + NOMAS_SPARSE_QUERY_BLOCK - 1) // NOMAS_SPARSE_QUERY_BLOCK
+    if block_list.dtype != torch.int32 or block_list.dim() != 3 or block_list.shape[:2] != (H, nqb):
+        raise ValueError(f"block_list must be int32 [{H}, {nqb}, n_select]")
+    n_select = block_list.shape[2]
+    block_list = block_list.contiguous()
+    if workspace is None:
+        nb = nomas_segment_attention_workspace_bytes(n_video, n_text, n_select * NOMAS_SPARSE_KEY_BLOCK, H, D,
+                                                     d.kv_dtype, n_splits)
+        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().nomas_segment_attention_sparse(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d),
+                                                ctypes.c_void_p(block_list.data_ptr()), n_select, op, ldo, lp, scale,
+                                                n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                                _stream(stream)))
     return out
 
 

@@ -181,3 +181,31 @@ def test_block_causal_rejects_before_launch():
     assert call(wsb=need - 1) == nomas.NOMAS_E_WORKSPACE
     assert call(ws=None) == nomas.NOMAS_E_WORKSPACE
     assert b"workspace" in L.nomas_last_error()
+
+
+def test_sparse_rejects_before_launch():
+    L, d, _ = _desc(dtype=0, heads=2, dim=64, tpf=24, cap=4)
+    d.frames_written = 4                        # 96 cached rows: 1 candidate block
+    assert L.nomas_sparse_candidates(96) == 1 and L.nomas_sparse_candidates(129) == 2
+    assert L.nomas_sparse_candidates(-1) == -1
+    p = ctypes.c_void_p(1 << 24)
+    ws = ctypes.c_void_p(1 << 26)
+    need = L.nomas_sparse_select_workspace_bytes(64, 96, 2, 64)
+    assert need > 0
+    assert L.nomas_sparse_select(p, 128, 64, ctypes.byref(d), 2, p, ws, need, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_sparse_select(p, 128, 64, ctypes.byref(d), -1, p, ws, need, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_sparse_select(p, 128, 64, ctypes.byref(d), 1, None, ws, need, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_sparse_select(p, 128, 64, ctypes.byref(d), 1, p, ws, need - 1, None) == nomas.NOMAS_E_WORKSPACE
+    assert L.nomas_sparse_select(p, 128, 64, ctypes.byref(d), 0, None, None, 0, None) == nomas.NOMAS_OK
+    wsb = L.nomas_segment_attention_workspace_bytes(48, 16, 128, 2, 64, 0, 0)
+
+    def att(**kw):
+        a = dict(lst=p, n=1, ws=ws, wsb=wsb)
+        a.update(kw)
+        return L.nomas_segment_attention_sparse(p, p, p, 128, 48, 16, ctypes.byref(d), a["lst"], a["n"], p, 128, None,
+                                                0.125, 0, a["ws"], a["wsb"], None)
+    assert att(n=2) == nomas.NOMAS_E_INVALID
+    assert att(n=-1) == nomas.NOMAS_E_INVALID
+    assert att(lst=None) == nomas.NOMAS_E_INVALID
+    assert att(lst=ctypes.c_void_p((1 << 24) + 2)) == nomas.NOMAS_E_INVALID
+    assert att(wsb=0) == nomas.NOMAS_E_WORKSPACE

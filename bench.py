@@ -13,9 +13,15 @@ Also reported (outside the timed steps):
     bf16 MFMA peak -> ``roofline``;
   * one multi-segment block-causal call at a training shape (4 segments x 7,936
     rows, 18-frame window) -> ``block_causal_tflops``;
+  * the layer shape under the sparse policy: selection of 34 of the 135
+    candidate blocks + sparse attention -> ``sparse_select_us``,
+    ``sparse_attention_ms``;
   * the full denoise sweep: 54 layers x 8 steps x 3 turns of RoPE + attention
     against per-layer INT8 18-frame windows, with the 54 appends after step 8
-    of each turn -> ``denoise_ms_per_step`` (median over the 24 steps);
+    of each turn -> ``denoise_ms_per_step`` (median over the 24 steps); and the
+    same turns under the sparse policy (steps 1-2 dense, then candidate-block
+    selection + attention to 25 % of the blocks) -> ``denoise_sparse_ms_per_step``
+    (mean over the 8 steps of a turn, averaged over turns);
   * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline``.
 Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
@@ -136,7 +142,13 @@ def denoise_bench(n_turns=3):
         caches.append(c)
     ws = nomas.workspace_for(caches[0], wl.n_video, wl.n_text)
     out = torch.empty((wl.n_q, H, D), dtype=torch.bfloat16, device="cuda")
-    step_ms, append_ms = [], []
+    # sparse policy: dense for steps 1-2, then 25 % of the candidate blocks
+    n_sel = (nomas.nomas_sparse_candidates(caches[0].n_cached) + 3) // 4
+    nqb = (wl.n_q + nomas.NOMAS_SPARSE_QUERY_BLOCK - 1) // nomas.NOMAS_SPARSE_QUERY_BLOCK
+    lists = torch.empty((H, nqb, n_sel), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(nomas.lib().nomas_sparse_select_workspace_bytes(wl.n_q, caches[0].n_cached, H, D),
+                         dtype=torch.uint8, device="cuda")
+    step_ms, append_ms, sparse_ms = [], [], []
     for turn in range(n_turns):
         qkv = [tuple(randn((wl.n_q, H, D), 1000 * layer + 100 * (turn + 1) + t) for t in range(3))
                for layer in range(L)]
@@ -152,6 +164,24 @@ def denoise_bench(n_turns=3):
             e1.record()
             torch.cuda.synchronize()
             step_ms.append(e0.elapsed_time(e1))
+        # the same turn under the sparse policy (RoPE is in place, so the sparse
+        # pass sees Q/K rotated once more than the dense one: same cost)
+        for s in range(S):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for layer in range(L):
+                q, k, v = qkv[layer]
+                nomas.nomas_rope3d(q, k, t0, F, wl.grid_h, wl.grid_w, wl.rope_split, H, D)
+                if s < 2:
+                    nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, caches[layer], out=out,
+                                                  workspace=ws)
+                else:
+                    nomas.nomas_sparse_select(q, wl.n_q, caches[layer], n_sel, block_list=lists, workspace=ws_sel)
+                    nomas.nomas_segment_attention_sparse(q, k, v, wl.n_video, wl.n_text, caches[layer], lists,
+                                                         out=out, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            sparse_ms.append(e0.elapsed_time(e1))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for layer in range(L):
@@ -159,15 +189,59 @@ def denoise_bench(n_turns=3):
         e1.record()
         torch.cuda.synchronize()
         append_ms.append(e0.elapsed_time(e1))
-        log(f"[bench] denoise turn {turn + 1}: median step {statistics.median(step_ms[-S:]):.2f} ms, "
-            f"appends {append_ms[-1]:.2f} ms")
+        log(f"[bench] denoise turn {turn + 1}: median step {statistics.median(step_ms[-S:]):.2f} ms, sparse policy "
+            f"{statistics.mean(sparse_ms[-S:]):.2f} ms/step on average, appends {append_ms[-1]:.2f} ms")
         del qkv
     flop_step = L * wl.attention_flop()
     med = statistics.median(step_ms)
     return dict(denoise_ms_per_step=med, denoise_tflops=flop_step / med / 1e9,
+                denoise_sparse_ms_per_step=statistics.mean(sparse_ms), denoise_sparse_n_select=n_sel,
                 denoise_append_ms_per_turn=statistics.mean(append_ms),
                 denoise_int8_append_bytes_per_layer=2 * wl.n_video * H * D * 2 + 2 * wl.n_video * H * D
                 + 2 * wl.n_video * H * 4)
+
+
+def sparse_layer_bench(reps=20):
+    """The single-layer bf16 shape under the sparse policy: candidate-block
+    selection (34 of the 135 blocks of 128 cached rows, 25 %) + sparse attention."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["layer_bf16"]
+    H, D = wl.n_heads, wl.head_dim
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, False)
+    kb, vb = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    out = torch.empty_like(q)
+    nc = nomas.nomas_sparse_candidates(cache.n_cached)
+    n_sel = (nc + 3) // 4
+    nqb = (wl.n_q + nomas.NOMAS_SPARSE_QUERY_BLOCK - 1) // nomas.NOMAS_SPARSE_QUERY_BLOCK
+    lists = torch.empty((H, nqb, n_sel), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(nomas.lib().nomas_sparse_select_workspace_bytes(wl.n_q, cache.n_cached, H, D),
+                         dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nomas.nomas_segment_attention_workspace_bytes(wl.n_video, wl.n_text, n_sel * 128, H, D, 0),
+                     dtype=torch.uint8, device="cuda")
+    sel = lambda: nomas.nomas_sparse_select(q, wl.n_q, cache, n_sel, block_list=lists, workspace=ws_sel)
+    att = lambda: nomas.nomas_segment_attention_sparse(q, k, v, wl.n_video, wl.n_text, cache, lists, out=out,
+                                                       workspace=ws)
+    times = {}
+    for name, fn in (("select", sel), ("attention", att)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / reps
+    flop = 4 * wl.n_q * (n_sel * 128 + wl.n_q) * D * H
+    log(f"[bench] sparse layer: select {times['select'] * 1e3:.1f} us, attention {times['attention']:.3f} ms "
+        f"({flop / times['attention'] / 1e9:.1f} TFLOP/s on the kept keys)")
+    return dict(sparse_select_us=round(times["select"] * 1e3, 2), sparse_attention_ms=round(times["attention"], 4),
+                sparse_attention_tflops=round(flop / times["attention"] / 1e9, 1), sparse_n_select=n_sel)
 
 
 def block_causal_bench(reps=20):
@@ -268,10 +342,13 @@ def main():
     )
     if not args.no_denoise:
         d = denoise_bench()
+        extra.update(denoise_sparse_ms_per_step=round(d["denoise_sparse_ms_per_step"], 3),
+                     denoise_sparse_n_select=d["denoise_sparse_n_select"])
         extra.update(denoise_ms_per_step=round(d["denoise_ms_per_step"], 3),
                      denoise_attention_tflops=round(d["denoise_tflops"], 1),
                      denoise_append_ms_per_turn=round(d["denoise_append_ms_per_turn"], 3))
     extra.update(block_causal_bench())
+    extra.update(sparse_layer_bench())
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
     line = {
         "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",

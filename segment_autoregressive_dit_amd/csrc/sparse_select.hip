@@ -21,50 +21,75 @@ constexpr int kSpKeyBlock = NOMAS_SPARSE_KEY_BLOCK;
 constexpr int kSpQueryBlock = NOMAS_SPARSE_QUERY_BLOCK;
 constexpr int kSpMaxCandidates = 8192;   // scores of one (query block, head) held in LDS
 
+// Row means: a thread takes 8 consecutive channels of one row per step (one
+// 16-byte load for bf16, 8 bytes for int8); D/8 threads cover a row and the
+// 256/(D/8) row groups are summed through LDS at the end.
+template <int D>
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], const u32x4 w) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] += bf16_lo(w[e]);
+    acc[2 * e + 1] += bf16_hi(w[e]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void finish_mean(float (&acc)[8], float* __restrict__ dst, int count) {
+  constexpr int TPR = D / 8, RG = 256 / TPR;
+  __shared__ float part[RG][D];
+  const int g = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][c0 + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) s += part[i][threadIdx.x];
+    dst[threadIdx.x] = s / (float)count;
+  }
+}
+
 // mean over the rows of query block b of head h: mq[h][b][d]
 template <int D>
 __global__ __launch_bounds__(256) void sp_mean_q_kernel(const uint16_t* __restrict__ q, int64_t ld, int n_q,
                                                         float* __restrict__ mq, int nqb) {
-  constexpr int RG = 256 / D;               // row groups per workgroup
-  __shared__ float part[RG][D];
+  constexpr int TPR = D / 8, RG = 256 / TPR;
   const int b = blockIdx.x, h = blockIdx.y;
-  const int d = threadIdx.x % D, g = threadIdx.x / D;
+  const int g = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * 8;
   const int r0 = b * kSpQueryBlock, r1 = min(n_q, r0 + kSpQueryBlock);
-  float acc = 0.f;
-  for (int r = r0 + g; r < r1; r += RG) acc += bf16_lo(q[(int64_t)r * ld + (int64_t)h * D + d]);
-  part[g][d] = acc;
-  __syncthreads();
-  if (g == 0) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < RG; ++i) s += part[i][d];
-    mq[((int64_t)h * nqb + b) * D + d] = s / (float)(r1 - r0);
-  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int r = r0 + g; r < r1; r += RG)
+    add_bf16x8<D>(acc, *reinterpret_cast<const u32x4*>(q + (int64_t)r * ld + (int64_t)h * D + c0));
+  finish_mean<D>(acc, mq + ((int64_t)h * nqb + b) * D, r1 - r0);
 }
 
-// mean over the keys of candidate block c of head h: mk[h][c][d]
+// mean over the keys of candidate block c of head h: mk[h][c][d] (INT8 keys as
+// code * scale)
 template <int D, bool I8>
 __global__ __launch_bounds__(256) void sp_mean_k_kernel(const void* __restrict__ kc, const float* __restrict__ ks,
                                                         int pitch, int n_cached, float* __restrict__ mk, int nc) {
-  constexpr int RG = 256 / D;
-  __shared__ float part[RG][D];
+  constexpr int TPR = D / 8, RG = 256 / TPR;
   const int c = blockIdx.x, h = blockIdx.y;
-  const int d = threadIdx.x % D, g = threadIdx.x / D;
+  const int g = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * 8;
   const int r0 = c * kSpKeyBlock, r1 = min(n_cached, r0 + kSpKeyBlock);
-  float acc = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int r = r0 + g; r < r1; r += RG) {
-    const int64_t i = ((int64_t)h * pitch + r) * D + d;
-    if (I8) acc += static_cast<float>(static_cast<const int8_t*>(kc)[i]) * ks[(int64_t)h * pitch + r];
-    else acc += bf16_lo(static_cast<const uint16_t*>(kc)[i]);
-  }
-  part[g][d] = acc;
-  __syncthreads();
-  if (g == 0) {
-    float s = 0.f;
+    const int64_t row = (int64_t)h * pitch + r;
+    if constexpr (I8) {
+      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(kc) + row * D + c0);
+      const float sc = ks[row];
 #pragma unroll
-    for (int i = 0; i < RG; ++i) s += part[i][d];
-    mk[((int64_t)h * nc + c) * D + d] = s / (float)(r1 - r0);
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += static_cast<float>(static_cast<int>(w.x << (24 - 8 * e)) >> 24) * sc;
+        acc[4 + e] += static_cast<float>(static_cast<int>(w.y << (24 - 8 * e)) >> 24) * sc;
+      }
+    } else {
+      add_bf16x8<D>(acc, *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(kc) + row * D + c0));
+    }
   }
+  finish_mean<D>(acc, mk + ((int64_t)h * nc + c) * D, r1 - r0);
 }
 
 // scores of all candidates for (query block b, head h), then the n_select best

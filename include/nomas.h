@@ -152,6 +152,39 @@ int32_t nomas_rope3d(uint16_t* q, uint16_t* k, int64_t ld, int32_t n_heads, int3
 int32_t nomas_kvcache_append(nomas_kvcache* c, const uint16_t* k_new, const uint16_t* v_new,
                              int64_t ld, int32_t n_frames, void* stream);
 
+/*
+ * Archive of frames leaving the window (the lifelong history the pages keep in
+ * CPU memory: "Persistent Lifelong KV Cache", madebyagents.com "Hy-Nomas";
+ * orcarouter.ai "Die Schleife"). Copies run on the DMA engines
+ * (hipMemcpy2DAsync on `stream`), asynchronous to the host: the host buffer must
+ * stay valid until the stream reaches them, and should be pinned
+ * (hipHostMalloc) for the copies to overlap with compute.
+ * A frame's record (nomas_kvcache_record_bytes) is its slot contents in cache
+ * order: K [n_heads][tpf][head_dim], then V^T [n_heads][head_dim][tpf] (int8
+ * codes or bf16 bits), then for INT8 the key scales [n_heads][tpf] and the
+ * value scales [n_heads][tpf] (float32).
+ */
+size_t nomas_kvcache_record_bytes(const nomas_kvcache* c);   /* 0 if c is invalid */
+
+/* Records of the retained frames [first_frame, first_frame + n_frames) (absolute
+ * frame numbers, as counted by frames_written) -> host_dst (host, n_frames
+ * records back to back). Frames that are not retained: NOMAS_E_INVALID. */
+int32_t nomas_kvcache_export_frames(const nomas_kvcache* c, int64_t first_frame, int32_t n_frames,
+                                    void* host_dst, void* stream);
+
+/* nomas_kvcache_append of 1 <= n_frames <= capacity frames that first exports
+ * the retained frames the append overwrites (the oldest ones) to host_evicted
+ * (host, room for n_frames records); *n_evicted (host) receives their count,
+ * they being frames [frames_written - valid, ... + *n_evicted) before the call. */
+int32_t nomas_kvcache_append_archive(nomas_kvcache* c, const uint16_t* k_new, const uint16_t* v_new,
+                                     int64_t ld, int32_t n_frames, void* host_evicted, int32_t* n_evicted,
+                                     void* stream);
+
+/* Appends 1 <= n_frames <= capacity archived records (host_src, back to back)
+ * to the cache unchanged, like nomas_kvcache_append (frames_written advances;
+ * the oldest frames are overwritten): e.g. to bring history back for attention. */
+int32_t nomas_kvcache_restore_frames(nomas_kvcache* c, const void* host_src, int32_t n_frames, void* stream);
+
 /* Workspace bytes nomas_segment_attention needs for these sizes, the cache's
  * kv_dtype (nomas_kv_dtype: it sets the key tile) and n_splits (0 = the
  * automatic choice, which depends only on these arguments, n_cached being the

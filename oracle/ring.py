@@ -25,6 +25,7 @@ class RingModel:
             raise ValueError("capacity must be >= 1")
         self.capacity = capacity_frames
         self.frames = []            # list of (absolute frame index, payload)
+        self.evicted = []           # frames that left the window, in order
         self.frames_written = 0
 
     def append(self, payloads):
@@ -33,7 +34,7 @@ class RingModel:
             self.frames.append((self.frames_written, p))
             self.frames_written += 1
             while len(self.frames) > self.capacity:
-                self.frames.pop(0)
+                self.evicted.append(self.frames.pop(0))
 
     def retained(self):
         """Retained (absolute index, payload) pairs, oldest first."""

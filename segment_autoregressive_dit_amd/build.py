@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnomas.so")
-SOURCES = ["nomas_host.cpp", "rope3d.hip", "kvcache_append.hip", "attention.hip", "sparse_select.hip"]
+SOURCES = ["nomas_host.cpp", "rope3d.hip", "kvcache_append.hip", "kvcache_archive.cpp", "attention.hip",
+           "sparse_select.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

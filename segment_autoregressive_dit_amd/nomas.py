@@ -77,6 +77,10 @@ def lib():
         "nomas_segment_attention": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp, sz, vp]),
         "nomas_block_causal_attention_workspace_bytes": (sz, [seg_p, i32, i32, i32, i32]),
         "nomas_sparse_candidates": (i32, [i64]),
+        "nomas_kvcache_record_bytes": (sz, [desc_p]),
+        "nomas_kvcache_export_frames": (i32, [desc_p, i64, i32, vp, vp]),
+        "nomas_kvcache_append_archive": (i32, [desc_p, vp, vp, i64, i32, vp, ctypes.POINTER(i32), vp]),
+        "nomas_kvcache_restore_frames": (i32, [desc_p, vp, i32, vp]),
         "nomas_sparse_select_workspace_bytes": (sz, [i32, i64, i32, i32]),
         "nomas_sparse_select": (i32, [vp, i64, i32, desc_p, i32, vp, vp, sz, vp]),
         "nomas_segment_attention_sparse": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i32, vp, i64, vp, f32, i32,
@@ -115,6 +119,11 @@ def _rows_view(t, name, heads, head_dim):
     else:
         raise ValueError(f"{name}: expected a 2-D or 3-D tensor")
     return ctypes.c_void_p(t.data_ptr()), t.stride(0)
+
+
+def _host_buffer(t, nbytes, name):
+    if t.device.type != "cpu" or t.dtype != torch.uint8 or not t.is_contiguous() or t.numel() < nbytes:
+        raise ValueError(f"{name} must be a contiguous uint8 host tensor of at least {nbytes} bytes")
 
 
 def nomas_version():
@@ -162,6 +171,40 @@ class KVCache:
     @property
     def n_cached(self):
         return self.valid_frames * self.desc.tokens_per_frame
+
+    def nomas_kvcache_record_bytes(self):
+        return lib().nomas_kvcache_record_bytes(ctypes.byref(self.desc))
+
+    def host_records(self, n_frames):
+        """A pinned host buffer for n_frames archive records."""
+        return torch.empty(max(1, n_frames) * self.nomas_kvcache_record_bytes(), dtype=torch.uint8, pin_memory=True)
+
+    def nomas_kvcache_export_frames(self, first_frame, n_frames, host_dst, stream=None):
+        """Records of retained frames [first_frame, +n_frames) -> host_dst (uint8 CPU tensor)."""
+        _host_buffer(host_dst, n_frames * self.nomas_kvcache_record_bytes(), "host_dst")
+        _check(lib().nomas_kvcache_export_frames(ctypes.byref(self.desc), first_frame, n_frames,
+                                                 ctypes.c_void_p(host_dst.data_ptr()), _stream(stream)))
+
+    def nomas_kvcache_append_archive(self, k_new, v_new, n_frames, host_evicted, stream=None):
+        """Append that first exports the frames it overwrites; returns their count."""
+        H, D = self.desc.n_heads, self.desc.head_dim
+        kp, ld = _rows_view(k_new, "k_new", H, D)
+        vp, ldv = _rows_view(v_new, "v_new", H, D)
+        if ld != ldv:
+            raise ValueError("k_new and v_new must share a row stride")
+        if k_new.shape[0] < n_frames * self.desc.tokens_per_frame:
+            raise ValueError("k_new/v_new hold fewer rows than n_frames frames")
+        _host_buffer(host_evicted, n_frames * self.nomas_kvcache_record_bytes(), "host_evicted")
+        n_ev = ctypes.c_int32(0)
+        _check(lib().nomas_kvcache_append_archive(ctypes.byref(self.desc), kp, vp, ld, n_frames,
+                                                  ctypes.c_void_p(host_evicted.data_ptr()), ctypes.byref(n_ev),
+                                                  _stream(stream)))
+        return n_ev.value
+
+    def nomas_kvcache_restore_frames(self, host_src, n_frames, stream=None):
+        _host_buffer(host_src, n_frames * self.nomas_kvcache_record_bytes(), "host_src")
+        _check(lib().nomas_kvcache_restore_frames(ctypes.byref(self.desc), ctypes.c_void_p(host_src.data_ptr()),
+                                                  n_frames, _stream(stream)))
 
     def nomas_kvcache_append(self, k_new, v_new, n_frames, stream=None):
         d = self.desc

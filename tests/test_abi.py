@@ -209,3 +209,24 @@ def test_sparse_rejects_before_launch():
     assert att(lst=None) == nomas.NOMAS_E_INVALID
     assert att(lst=ctypes.c_void_p((1 << 24) + 2)) == nomas.NOMAS_E_INVALID
     assert att(wsb=0) == nomas.NOMAS_E_WORKSPACE
+
+
+def test_archive_rejects_before_launch():
+    L, d, _ = _desc(dtype=1, heads=2, dim=64, tpf=24, cap=4)
+    rec = L.nomas_kvcache_record_bytes(ctypes.byref(d))
+    assert rec == 2 * 24 * 64 * 2 + 2 * 2 * 24 * 4
+    d.frames_written = 6                                   # retained frames 2..5
+    host = ctypes.create_string_buffer(rec * 4)
+    assert L.nomas_kvcache_export_frames(ctypes.byref(d), 1, 1, host, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_export_frames(ctypes.byref(d), 5, 2, host, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_export_frames(ctypes.byref(d), 2, 1, None, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_export_frames(ctypes.byref(d), 3, 0, None, None) == nomas.NOMAS_OK
+    n = ctypes.c_int32(-1)
+    p = ctypes.c_void_p(1 << 24)
+    assert L.nomas_kvcache_append_archive(ctypes.byref(d), p, p, 128, 5, host, ctypes.byref(n), None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_append_archive(ctypes.byref(d), p, p, 128, 2, host, None, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_append_archive(ctypes.byref(d), p, p, 64, 2, host, ctypes.byref(n), None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_append_archive(ctypes.byref(d), p, p, 128, 2, None, ctypes.byref(n), None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_restore_frames(ctypes.byref(d), host, 0, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_kvcache_restore_frames(ctypes.byref(d), None, 1, None) == nomas.NOMAS_E_INVALID
+    assert d.frames_written == 6 and n.value == -1

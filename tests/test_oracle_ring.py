@@ -2,6 +2,8 @@
 
 from hypothesis import given, settings, strategies as st
 
+import numpy as np
+
 from oracle.ring import RingModel
 
 
@@ -32,3 +34,19 @@ def test_append_larger_than_capacity_keeps_tail():
     r.append(list(range(10)))
     assert [p for _, p in r.retained()] == [6, 7, 8, 9]
     assert r.expected_slots() == {2: (6, 6), 3: (7, 7), 0: (8, 8), 1: (9, 9)}
+
+
+def test_evicted_then_retained_is_every_frame_in_order():
+    # every appended frame either left the window (in append order) or is retained
+    rng = np.random.default_rng(7)
+    for cap in (1, 3, 4, 18):
+        ring = RingModel(cap)
+        total = 0
+        for _ in range(12):
+            n = int(rng.integers(1, 2 * cap + 1))
+            ring.append([total + i for i in range(n)])
+            total += n
+            seen = [f for f, _ in ring.evicted] + [f for f, _ in ring.retained()]
+            assert seen == list(range(total))
+            assert all(p == f for f, p in ring.evicted)
+            assert len(ring.evicted) == max(0, total - cap)

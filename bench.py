@@ -13,6 +13,9 @@ Also reported (outside the timed steps):
     bf16 MFMA peak -> ``roofline``;
   * one multi-segment block-causal call at a training shape (4 segments x 7,936
     rows, 18-frame window) -> ``block_causal_tflops``;
+  * the evicted-frame archive: 8 INT8 frame records of one layer window to
+    pinned host memory and back by the copy engines -> ``archive_d2h_gbps``,
+    ``archive_h2d_gbps``;
   * the layer shape under the sparse policy: selection of 34 of the 135
     candidate blocks + sparse attention -> ``sparse_select_us``,
     ``sparse_attention_ms``;
@@ -244,6 +247,39 @@ def sparse_layer_bench(reps=20):
                 sparse_attention_tflops=round(flop / times["attention"] / 1e9, 1), sparse_n_select=n_sel)
 
 
+def archive_bench(reps=10):
+    """Host archive of evicted frames: one INT8 layer window (18 frames of the
+    24x40 grid, 16x128 heads); the 8 frames a segment evicts are exported to
+    pinned host memory, and restored back, by the copy engines."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["denoise_int8"]
+    H, D, tpf, F = wl.n_heads, wl.head_dim, wl.tpf, wl.seg_frames
+    cache = nomas.KVCache(H, D, tpf, wl.capacity_frames, True)
+    n = wl.cached_frames * tpf
+    cache.nomas_kvcache_append(dev_bf16(synth.normal_bf16((n, H, D), 78, 0, 0, 3)),
+                               dev_bf16(synth.normal_bf16((n, H, D), 78, 0, 0, 4)), wl.cached_frames)
+    host = cache.host_records(F)
+    rec = cache.nomas_kvcache_record_bytes()
+    first = cache.frames_written - cache.valid_frames
+    res = {}
+    for name, fn in (("d2h", lambda: cache.nomas_kvcache_export_frames(first, F, host)),
+                     ("h2d", lambda: cache.nomas_kvcache_restore_frames(host, F))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / reps
+        res[name] = F * rec / dt / 1e9
+    log(f"[bench] archive: {F} frames x {rec / 1e6:.2f} MB records, D2H {res['d2h']:.1f} GB/s, "
+        f"H2D {res['h2d']:.1f} GB/s")
+    return dict(archive_record_mb=round(rec / 1e6, 3), archive_d2h_gbps=round(res["d2h"], 1),
+                archive_h2d_gbps=round(res["h2d"], 1))
+
+
 def block_causal_bench(reps=20):
     """Multi-segment call at a training shape: 4 segments of 8 frames on the
     24x40 grid + 256 text rows each (31,744 rows), 16x128 heads, 18-frame window."""
@@ -349,6 +385,7 @@ def main():
                      denoise_append_ms_per_turn=round(d["denoise_append_ms_per_turn"], 3))
     extra.update(block_causal_bench())
     extra.update(sparse_layer_bench())
+    extra.update(archive_bench())
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
     line = {
         "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",

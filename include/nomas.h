@@ -230,6 +230,39 @@ int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * 3D RoPE angles of a segment's video rows as a table, for the fused projection
+ * below (computed once per segment, reused by every layer and step):
+ * table[i][p] = (cos, sin)(pos * theta^(-2j/d)) of pair p (band and law as in
+ * nomas_rope3d, angle negated when inverse != 0) for video row i of the
+ * segment. table: (device) float32 [n_frames*grid_h*grid_w][head_dim/2][2],
+ * 8-byte aligned. Same angle arithmetic as nomas_rope3d (float32 pos*w, sincosf).
+ */
+int32_t nomas_rope3d_table(float* table, int32_t head_dim, int32_t t0, int32_t n_frames, int32_t grid_h,
+                           int32_t grid_w, int32_t d_t, int32_t d_h, int32_t d_w, float theta, int32_t inverse,
+                           void* stream);
+
+/*
+ * QKV projection of a DiT block with the 3D RoPE of the video rows fused in:
+ * qkv[r, c] = bf16( (x[r, :] . w[c, :]) rotated ) for the 3*n_heads*head_dim
+ * channels c = [query | key | value] (head h's head_dim channels together in
+ * each part). The query and key channels of rows r < n_video are rotated in
+ * pairs (2j, 2j+1) of each head by rope_table[r][j] (nomas_rope3d_table);
+ * text rows (r >= n_video), value channels, and every row when rope_table is
+ * NULL are not. No bias. Pages: hidden size 2,048, 16 heads of 128, 3D RoPE
+ * ("Hy-Nomas auf einer RTX 4090", inferencekey.com, "Modell und Dateien").
+ * Arithmetic: bf16 MFMA products, float32 accumulation and rotation, one
+ * rounding to bf16.
+ * x: (device) bf16 [n_rows][ld_x]; w: (device) bf16 [3*n_heads*head_dim][ld_w];
+ * hidden a positive multiple of 64, ld_x and ld_w >= hidden and multiples of 8;
+ * qkv: (device) bf16 [n_rows][ld_qkv], ld_qkv >= 3*n_heads*head_dim and a
+ * multiple of 4 (q, k, v for nomas_segment_attention are views at column
+ * offsets 0, H*D, 2*H*D with ld_qkv as their row stride). No workspace.
+ */
+int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden, const uint16_t* w,
+                             int64_t ld_w, int32_t n_heads, int32_t head_dim, int32_t n_video,
+                             const float* rope_table, uint16_t* qkv, int64_t ld_qkv, void* stream);
+
+/*
  * Block-sparse segment attention. After two dense denoising steps the pages keep
  * 25 % of the candidate video blocks ("Hy-Nomas auf einer RTX 4090",
  * inferencekey.com, "Das Single-GPU-Preset", citing the tech report's 6.2); they

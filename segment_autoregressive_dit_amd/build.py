@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnomas.so")
 SOURCES = ["nomas_host.cpp", "rope3d.hip", "kvcache_append.hip", "kvcache_archive.cpp", "attention.hip",
-           "sparse_select.hip"]
+           "sparse_select.hip", "qkv_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

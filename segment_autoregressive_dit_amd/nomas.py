@@ -77,6 +77,8 @@ def lib():
         "nomas_segment_attention": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp, sz, vp]),
         "nomas_block_causal_attention_workspace_bytes": (sz, [seg_p, i32, i32, i32, i32]),
         "nomas_sparse_candidates": (i32, [i64]),
+        "nomas_rope3d_table": (i32, [vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]),
+        "nomas_qkv_projection": (i32, [vp, i64, i32, i32, vp, i64, i32, i32, i32, vp, vp, i64, vp]),
         "nomas_kvcache_record_bytes": (sz, [desc_p]),
         "nomas_kvcache_export_frames": (i32, [desc_p, i64, i32, vp, vp]),
         "nomas_kvcache_append_archive": (i32, [desc_p, vp, vp, i64, i32, vp, ctypes.POINTER(i32), vp]),
@@ -389,3 +391,43 @@ def nomas_block_causal_attention(q, k, v, segments, tokens_per_frame, window_fra
                                               H, D, op, ldo, lp, scale, ctypes.c_void_p(workspace.data_ptr()),
                                               workspace.numel(), _stream(stream)))
     return out
+
+
+def nomas_rope3d_table(head_dim, t0, n_frames, grid_h, grid_w, band, theta=10000.0, inverse=False, table=None,
+                       stream=None):
+    """(cos, sin) table [n_frames*grid_h*grid_w, head_dim/2, 2] float32 of a segment's video rows."""
+    n = n_frames * grid_h * grid_w
+    if table is None:
+        table = torch.empty((n, head_dim // 2, 2), dtype=torch.float32, device="cuda")
+    if table.dtype != torch.float32 or not table.is_cuda or not table.is_contiguous() or table.numel() < n * head_dim:
+        raise ValueError("table must be a contiguous float32 CUDA tensor of n_rows*head_dim elements")
+    d_t, d_h, d_w = band
+    _check(lib().nomas_rope3d_table(ctypes.c_void_p(table.data_ptr()), head_dim, t0, n_frames, grid_h, grid_w, d_t,
+                                    d_h, d_w, float(theta), int(bool(inverse)), _stream(stream)))
+    return table
+
+
+def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qkv=None, stream=None):
+    """qkv = [q | k | v] projection of x [n, hidden] by w [3*H*D, hidden] with RoPE
+    on the video rows' q, k (when a table is given). Returns qkv [n, 3*H*D]."""
+    for t, name in ((x, "x"), (w, "w")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor with unit inner stride")
+    n, hidden = x.shape
+    n_ch = 3 * n_heads * head_dim
+    if w.shape[0] != n_ch or w.shape[1] != hidden:
+        raise ValueError(f"w must be [{n_ch}, {hidden}]")
+    if qkv is None:
+        qkv = torch.empty((n, n_ch), dtype=torch.bfloat16, device=x.device)
+    if qkv.dtype != torch.bfloat16 or qkv.dim() != 2 or qkv.stride(1) != 1 or qkv.shape[0] < n or qkv.shape[1] < n_ch:
+        raise ValueError("qkv must be a 2-D bfloat16 tensor of at least [n, 3*H*D] with unit inner stride")
+    tp = None
+    if rope_table is not None:
+        if rope_table.dtype != torch.float32 or not rope_table.is_contiguous() or \
+                rope_table.numel() < n_video * head_dim:
+            raise ValueError("rope_table must be a contiguous float32 tensor of n_video*head_dim elements")
+        tp = ctypes.c_void_p(rope_table.data_ptr())
+    _check(lib().nomas_qkv_projection(ctypes.c_void_p(x.data_ptr()), x.stride(0), n, hidden,
+                                      ctypes.c_void_p(w.data_ptr()), w.stride(0), n_heads, head_dim, n_video, tp,
+                                      ctypes.c_void_p(qkv.data_ptr()), qkv.stride(0), _stream(stream)))
+    return qkv

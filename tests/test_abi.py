@@ -230,3 +230,24 @@ def test_archive_rejects_before_launch():
     assert L.nomas_kvcache_restore_frames(ctypes.byref(d), host, 0, None) == nomas.NOMAS_E_INVALID
     assert L.nomas_kvcache_restore_frames(ctypes.byref(d), None, 1, None) == nomas.NOMAS_E_INVALID
     assert d.frames_written == 6 and n.value == -1
+
+
+def test_qkv_projection_rejects_before_launch():
+    L = nomas.lib()
+    p = ctypes.c_void_p(1 << 24)
+    ok = dict(x=p, ldx=2048, n=100, hid=2048, w=p, ldw=2048, H=16, D=128, nv=0, tab=None, y=p, ldy=6144)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.nomas_qkv_projection(a["x"], a["ldx"], a["n"], a["hid"], a["w"], a["ldw"], a["H"], a["D"], a["nv"],
+                                      a["tab"], a["y"], a["ldy"], None)
+    assert call(hid=2000) == nomas.NOMAS_E_INVALID           # not a multiple of 64
+    assert call(ldx=2040) == nomas.NOMAS_E_INVALID
+    assert call(ldy=6140) == nomas.NOMAS_E_INVALID
+    assert call(nv=101) == nomas.NOMAS_E_INVALID
+    assert call(D=96) == nomas.NOMAS_E_UNSUPPORTED
+    assert call(x=None) == nomas.NOMAS_E_INVALID
+    assert call(tab=ctypes.c_void_p((1 << 24) + 4)) == nomas.NOMAS_E_INVALID
+    assert L.nomas_rope3d_table(p, 128, 0, 1, 2, 2, 32, 48, 40, 10000.0, 0, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_rope3d_table(None, 128, 0, 1, 2, 2, 32, 48, 48, 10000.0, 0, None) == nomas.NOMAS_E_INVALID

@@ -16,6 +16,8 @@ Also reported (outside the timed steps):
   * the evicted-frame archive: 8 INT8 frame records of one layer window to
     pinned host memory and back by the copy engines -> ``archive_d2h_gbps``,
     ``archive_h2d_gbps``;
+  * the fused QKV projection + RoPE of the layer (7,936 x 2,048 -> 6,144)
+    -> ``qkv_tflops``;
   * the layer shape under the sparse policy: selection of 34 of the 135
     candidate blocks + sparse attention -> ``sparse_select_us``,
     ``sparse_attention_ms``;
@@ -43,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+H_HIDDEN = 2048                 # DiT hidden size
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_layer_bf16_hbm_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "segment_autoregressive_dit_amd", "csrc", "attention.hip")
 
@@ -247,6 +250,35 @@ def sparse_layer_bench(reps=20):
                 sparse_attention_tflops=round(flop / times["attention"] / 1e9, 1), sparse_n_select=n_sel)
 
 
+def qkv_bench(reps=20):
+    """The QKV projection of one layer at the single-layer shape with the RoPE
+    epilogue: 7,936 rows x hidden 2,048 -> 3 x 16 x 128 channels."""
+    import numpy as np
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["layer_bf16"]
+    H, D, hidden = wl.n_heads, wl.head_dim, H_HIDDEN
+    x = dev_bf16(synth.normal_bf16((wl.n_q, 1, hidden), 79, 0, 0, 0)[:, 0])
+    w = torch.randn((3 * H * D, hidden), device="cuda", dtype=torch.float32).div_(math.sqrt(hidden)).to(torch.bfloat16)
+    y = torch.empty((wl.n_q, 3 * H * D), dtype=torch.bfloat16, device="cuda")
+    table = nomas.nomas_rope3d_table(D, wl.t0, wl.seg_frames, wl.grid_h, wl.grid_w, wl.rope_split)
+    fn = lambda: nomas.nomas_qkv_projection(x, w, H, D, n_video=wl.n_video, rope_table=table, qkv=y)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = 2 * wl.n_q * hidden * 3 * H * D
+    log(f"[bench] qkv projection + RoPE: {ms * 1e3:.1f} us, {flop / ms / 1e9:.1f} TFLOP/s")
+    return dict(qkv_us=round(ms * 1e3, 2), qkv_tflops=round(flop / ms / 1e9, 1))
+
+
 def archive_bench(reps=10):
     """Host archive of evicted frames: one INT8 layer window (18 frames of the
     24x40 grid, 16x128 heads); the 8 frames a segment evicts are exported to
@@ -386,6 +418,7 @@ def main():
     extra.update(block_causal_bench())
     extra.update(sparse_layer_bench())
     extra.update(archive_bench())
+    extra.update(qkv_bench())
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
     line = {
         "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",

@@ -235,7 +235,7 @@ int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const 
  * table[i][p] = (cos, sin)(pos * theta^(-2j/d)) of pair p (band and law as in
  * nomas_rope3d, angle negated when inverse != 0) for video row i of the
  * segment. table: (device) float32 [n_frames*grid_h*grid_w][head_dim/2][2],
- * 8-byte aligned. Same angle arithmetic as nomas_rope3d (float32 pos*w, sincosf).
+ * 16-byte aligned. Same angle arithmetic as nomas_rope3d (float32 pos*w, sincosf).
  */
 int32_t nomas_rope3d_table(float* table, int32_t head_dim, int32_t t0, int32_t n_frames, int32_t grid_h,
                            int32_t grid_w, int32_t d_t, int32_t d_h, int32_t d_w, float theta, int32_t inverse,
@@ -248,7 +248,7 @@ int32_t nomas_rope3d_table(float* table, int32_t head_dim, int32_t t0, int32_t n
  * each part). The query and key channels of rows r < n_video are rotated in
  * pairs (2j, 2j+1) of each head by rope_table[r][j] (nomas_rope3d_table);
  * text rows (r >= n_video), value channels, and every row when rope_table is
- * NULL are not. No bias. Pages: hidden size 2,048, 16 heads of 128, 3D RoPE
+ * NULL are not (rope_table 16-byte aligned). No bias. Pages: hidden size 2,048, 16 heads of 128, 3D RoPE
  * ("Hy-Nomas auf einer RTX 4090", inferencekey.com, "Modell und Dateien").
  * Arithmetic: bf16 MFMA products, float32 accumulation and rotation, one
  * rounding to bf16.

@@ -229,7 +229,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     blist = a.blist + ((int64_t)h * a.nqb_sp + qt * C::BR / kSpQueryBlock) * a.n_sel;
     tiles_c_b = full_c_b = 0;
     if (a.n_sel > 0) {
-      const int rem = max(0, min(kSpKeyBlock, a.n_cached - blist[a.n_sel - 1] * kSpKeyBlock));
+      const int last = __builtin_amdgcn_readfirstlane(blist[a.n_sel - 1]);
+      const int rem = max(0, min(kSpKeyBlock, a.n_cached - last * kSpKeyBlock));
       tiles_c_b = (a.n_sel - 1) * TPB + (rem + BC - 1) / BC;
       full_c_b = (a.n_sel - 1) * TPB + rem / BC;
     }
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       return;
     }
     cache = t < tiles_c_b;
-    if (SP && cache) key0 = blist[t / TPB] * kSpKeyBlock + (t % TPB) * BC;
+    // (the list entry is the same for the whole block: keep it scalar)
+    if (SP && cache) key0 = __builtin_amdgcn_readfirstlane(blist[t / TPB]) * kSpKeyBlock + (t % TPB) * BC;
     else key0 = (cache ? t : t - tiles_c_b) * BC;
     nvalid = min(BC, (cache ? a.n_cached : a.n_cur) - key0);
   };

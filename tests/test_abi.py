@@ -248,6 +248,6 @@ def test_qkv_projection_rejects_before_launch():
     assert call(nv=101) == nomas.NOMAS_E_INVALID
     assert call(D=96) == nomas.NOMAS_E_UNSUPPORTED
     assert call(x=None) == nomas.NOMAS_E_INVALID
-    assert call(tab=ctypes.c_void_p((1 << 24) + 4)) == nomas.NOMAS_E_INVALID
+    assert call(tab=ctypes.c_void_p((1 << 24) + 8)) == nomas.NOMAS_E_INVALID
     assert L.nomas_rope3d_table(p, 128, 0, 1, 2, 2, 32, 48, 40, 10000.0, 0, None) == nomas.NOMAS_E_INVALID
     assert L.nomas_rope3d_table(None, 128, 0, 1, 2, 2, 32, 48, 48, 10000.0, 0, None) == nomas.NOMAS_E_INVALID

@@ -5,6 +5,7 @@ workload (for use under ``rocprofv3``)::
 
     python -m segment_autoregressive_dit_amd.profile_workload run --kernel attention --workload layer_bf16 --reps 5
     python -m segment_autoregressive_dit_amd.profile_workload run --kernel copy --bytes 1073741824
+    python -m segment_autoregressive_dit_amd.profile_workload run --kernel qkv --workload layer_bf16
 
 ``--kernel copy`` runs a plain streaming kernel of known size (torch's elementwise
 negation of a float32 buffer: reads N bytes, writes N bytes), the calibration for
@@ -48,6 +49,18 @@ def cmd_run(a):
         return
     wl = synth.WORKLOADS[a.workload]
     H, D = wl.n_heads, wl.head_dim
+    if a.kernel == "qkv":
+        hidden = H * D
+        x = _dev(synth.normal_bf16((wl.n_q, 1, hidden), 79, 0, 0, 0)[:, 0])
+        w = _dev(synth.normal_bf16((3 * H * D, 1, hidden), 79, 0, 0, 1)[:, 0])
+        table = nomas.nomas_rope3d_table(D, wl.t0, wl.seg_frames, wl.grid_h, wl.grid_w, wl.rope_split)
+        y = torch.empty((wl.n_q, 3 * H * D), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(a.reps):
+            nomas.nomas_qkv_projection(x, w, H, D, n_video=wl.n_video, rope_table=table, qkv=y)
+        torch.cuda.synchronize()
+        print(f"qkv on {a.workload}: {a.reps} launches", file=sys.stderr)
+        return
     cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, wl.kv_int8)
     kb, vb = synth.prefill_kv(wl)
     cache.nomas_kvcache_append(_dev(kb), _dev(vb), wl.cached_frames)
@@ -147,7 +160,7 @@ def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--kernel", choices=["attention", "rope", "append", "copy"], required=True)
+    r.add_argument("--kernel", choices=["attention", "rope", "append", "qkv", "copy"], required=True)
     r.add_argument("--workload", default="layer_bf16")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--splits", type=int, default=0)

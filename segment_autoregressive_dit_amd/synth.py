@@ -109,9 +109,11 @@ def outlier_channels(wl, layer=0):
                      for _ in range(wl.n_heads)]) if wl.k_outliers else None
 
 
-def normal_bf16(shape, wid, layer, turn, tid, outliers=None, out_scale=20.0):
-    """uint16 bf16 patterns of N(0,1) draws of ``shape`` = [rows, H, D]."""
+def normal_bf16(shape, wid, layer, turn, tid, outliers=None, out_scale=20.0, std=1.0):
+    """uint16 bf16 patterns of N(0, std^2) draws of ``shape`` = [rows, H, D]."""
     x = rng_for(wid, layer, turn, tid).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
     if outliers is not None:
         for h in range(shape[1]):
             x[:, h, outliers[h]] *= np.float32(out_scale)

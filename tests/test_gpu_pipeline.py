@@ -1,0 +1,82 @@
+"""One DiT block's attention path end to end, as a caller chains it: fused QKV
+projection with RoPE into one [q | k | v] buffer, segment attention on strided
+views of it (row stride 3*H*D) against the ring cache, then the append of the
+segment's K/V views. Three segments; every stage against the oracle chain
+(oracle/qkv.py -> oracle/attention.py, with oracle/quant.py and oracle/ring.py
+for the cache)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, quant, qkv
+from oracle.ring import RingModel
+from segment_autoregressive_dit_amd import nomas, synth
+
+from _gpu_util import cache_slots, dev_bf16, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_projection_attention_append_chain(int8):
+    H, D, hidden, gh, gw, F, T, W = 2, 128, 256, 6, 8, 2, 24, 3
+    tpf, nv = gh * gw, F * gh * gw
+    n = nv + T
+    band = (32, 48, 48)
+    rng = np.random.default_rng(21)
+    wb = synth._round_bf16_bits((rng.standard_normal((3 * H * D, hidden)) / math.sqrt(hidden)).astype(np.float32))
+    w64 = synth.bf16_bits_to_f64(wb)
+    cache = nomas.KVCache(H, D, tpf, W, int8)
+    ring = RingModel(W)
+    for s in range(3):
+        t0 = F * s
+        say(f"pipeline: int8={int8} segment {s}")
+        xb = synth.normal_bf16((n, 1, hidden), 97, s, 0, 0)[:, 0]
+        table = nomas.nomas_rope3d_table(D, t0, F, gh, gw, band)
+        y = nomas.nomas_qkv_projection(dev_bf16(xb), dev_bf16(wb), H, D, n_video=nv, rope_table=table)
+        q, k, v = (y[:, i * H * D:(i + 1) * H * D] for i in range(3))     # views, row stride 3*H*D
+        out = nomas.nomas_segment_attention(q, k, v, nv, T, cache)
+        cache.nomas_kvcache_append(k, v, F)
+        torch.cuda.synchronize()
+        # oracle chain
+        r = dict(t0=t0, n_frames=F, grid_h=gh, grid_w=gw, d_t=band[0], d_h=band[1], d_w=band[2])
+        oq, ok_, ov = qkv.qkv_projection(synth.bf16_bits_to_f64(xb), w64, H, D, n_video=nv, rope=r)
+        got_qkv = host_f64(y)
+        ref_qkv = np.concatenate([t.reshape(n, -1) for t in (oq, ok_, ov)], 1)
+        mag = np.abs(synth.bf16_bits_to_f64(xb)) @ np.abs(w64).T
+        pair = np.maximum(mag, mag.reshape(n, -1, 2)[:, :, ::-1].reshape(n, -1))
+        from oracle import formats
+        assert np.all(np.abs(got_qkv - ref_qkv) <= formats.bf16_ulp(ref_qkv) + 2.0 ** -12 * pair)
+        # attention on the GPU's own projections (its rounding is not the
+        # attention's to answer for), against the ring's retained frames
+        gq, gk, gv = (got_qkv[:, i * H * D:(i + 1) * H * D].reshape(n, H, D) for i in range(3))
+        frames = ring.retained()
+        kp = vp = None
+        if frames:
+            kp = np.concatenate([p[0] for _, p in frames], 0)
+            vp = np.concatenate([p[1] for _, p in frames], 0)
+        ref, _ = attention.segment_attention(gq, gk, gv, kp, vp, 1 / math.sqrt(D))
+        diff = np.abs(host_f64(out) - ref)
+        assert diff.max() <= 1e-2 * np.abs(ref).max() and diff.mean() <= 1e-3
+        # the cache as the oracle quantiser / ring lay it out
+        fr = []
+        for f in range(F):
+            kf, vf = gk[f * tpf:(f + 1) * tpf], gv[f * tpf:(f + 1) * tpf]
+            if int8:
+                kf, vf = quant.dequantise(*quant.quantise(kf)), quant.dequantise(*quant.quantise(vf))
+            fr.append((kf, vf))
+        ring.append(fr)
+        assert cache.frames_written == ring.frames_written
+    # final cache contents, slot by slot
+    kc, vc, ks, vs = cache_slots(cache)
+    for f, (kf, vf) in ring.retained():
+        slot = (f % W) * tpf
+        if int8:
+            got_k = kc[slot:slot + tpf].astype(np.float64) * ks[slot:slot + tpf, :, None]
+            got_v = vc[slot:slot + tpf].astype(np.float64) * vs[slot:slot + tpf, :, None]
+        else:
+            got_k, got_v = synth.bf16_bits_to_f64(kc[slot:slot + tpf]), synth.bf16_bits_to_f64(vc[slot:slot + tpf])
+        assert np.array_equal(got_k, kf) and np.array_equal(got_v, vf)

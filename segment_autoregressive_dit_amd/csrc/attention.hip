@@ -26,9 +26,10 @@
 //  * Online softmax in the log2 domain with a fixed reference max per query that
 //    is only raised when a tile's max exceeds it by more than kTau (probabilities
 //    stay <= 2^kTau, exact in fp32 and bf16 range), so the O rescale is rare.
-//  * INT8 cache tiles are staged through registers: key codes are converted to
-//    bf16 exactly and the key scale multiplies the fp32 logit of its key; values
-//    are dequantised (code * scale, rounded once to bf16) on the way into LDS.
+//  * INT8 cache tiles stage their codes through registers: key codes are
+//    converted to bf16 exactly and the key scale multiplies the fp32 logit of
+//    its key; values are dequantised (code * scale, rounded once to bf16) on the
+//    way into LDS. The scales themselves go global -> LDS by the load unit.
 //  * Split-KV: the key tiles are cut into contiguous chunks; each block writes a
 //    normalised fp32 partial and its log-sum-exp, merged in fixed order.
 //  * Block ids are remapped so the blocks that the hardware places on one XCD
@@ -184,7 +185,10 @@ struct AttnCfg {
   static constexpr int KSTAGE = KT_BYTES + BC * 4; // K tile + the tile's per-key K scales
   static constexpr int VSTAGE = VT_BYTES;          // V^T tile
   static constexpr int NVS = PIPE && VPF ? 3 : 2;  // V^T stages
-  static constexpr int LDS_BYTES = 2 * KSTAGE + NVS * VSTAGE;
+  // INT8: each wave's own copy of a tile's value scales
+  static constexpr int VSC_OFF = 2 * KSTAGE + NVS * VSTAGE;
+  static constexpr int VSC_BYTES = I8 ? NW * BC * 4 : 0;
+  static constexpr int LDS_BYTES = VSC_OFF + VSC_BYTES;
   static constexpr int NK8 = BC * D / 16 / NT;     // int8 K chunks (16 codes) per thread
   static constexpr int NV8 = D * BC / 16 / NT;     // int8 V chunks per thread
   static constexpr int BR = NW * QB * 16;          // queries per block
@@ -194,6 +198,8 @@ struct AttnCfg {
   static constexpr int VI = VT_BYTES / 1024 / NW;  // (V^T)
   static_assert(KT_BYTES % (1024 * NW) == 0 && VT_BYTES % (1024 * NW) == 0, "tile must split into 1 KB copies");
   static_assert((BC * D / 16) % NT == 0 && NK8 >= 1 && NV8 >= 1, "int8 tile must split evenly over threads");
+  static_assert(BC % 64 == 0, "scales are copied 64 keys per instruction");
+  static_assert(NT % (BC / 16) == 0, "a lane's int8 value chunks share their keys");
 };
 
 // MODE: kModeCached (a segment against the cache), kModeSegments (multi-segment
@@ -296,42 +302,51 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const __amdgpu_buffer_rsrc_t rvs_c = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(a.vs) + (int64_t)h * a.pitch_c, (short)0, I8 ? a.n_cached * 4 : 0, 0x00020000);
 
-  // INT8 cache tiles are staged through registers (codes, plus the scales they
-  // need: one per key for K, sixteen per value chunk); every other tile is
-  // copied global -> LDS by the load unit itself.
+  // bf16 tiles are copied global -> LDS by the load unit straight into their
+  // swizzled places. INT8 cache tiles: the codes are staged through registers
+  // (16 per lane per piece) and expanded into place by the lane that loaded
+  // them; the key scales are copied by the load unit straight to the stage,
+  // and each wave copies the value scales it needs to its own LDS slot.
   u32x4 stk[I8 ? C::NK8 : 1], stv[I8 ? C::NV8 : 1];
-  float sks = 0.f;
-  f32x4 svs[I8 ? C::NV8 : 1][4];
+  // (LDS copy targets are formed from scalar values where they are used, so
+  // that the copy's base address is known to be uniform)
+  auto vsc = [&]() { return lds + C::VSC_OFF + wave * BC * 4; };
 
   // MS: the key range [kbase, kend) of the joint sequence being visited
   int kbase = 0, kend = 0;
-  // tile t -> (is cache tile, first key inside its part, valid keys)
-  auto tile_info = [&](int t, bool& cache, int& key0, int& nvalid) {
+  // Every run of tiles is of one kind, known at compile time: cache tiles
+  // (cache_tag true) or tiles of the current segment / joint sequence.
+  // tile t -> (first key inside its part, valid keys)
+  auto tile_info = [&](int t, auto cache_tag, int& key0, int& nvalid) {
+    constexpr bool CACHE = decltype(cache_tag)::value;
     if constexpr (MS) {
-      cache = false;
       key0 = kbase + t * BC;
       nvalid = min(BC, kend - key0);
       return;
     }
-    cache = t < tiles_c_b;
     // (the list entry is the same for the whole block: keep it scalar)
-    if (SP && cache) key0 = __builtin_amdgcn_readfirstlane(blist[t / TPB]) * kSpKeyBlock + (t % TPB) * BC;
-    else key0 = (cache ? t : t - tiles_c_b) * BC;
-    nvalid = min(BC, (cache ? a.n_cached : a.n_cur) - key0);
+    if (SP && CACHE) key0 = __builtin_amdgcn_readfirstlane(blist[t / TPB]) * kSpKeyBlock + (t % TPB) * BC;
+    else key0 = __builtin_amdgcn_readfirstlane((CACHE ? t : t - tiles_c_b) * BC);
+    nvalid = min(BC, (CACHE ? a.n_cached : a.n_cur) - key0);
   };
 
   // ---- issue the loads of tile t's keys / values into K / V buffer i
-  auto start_k = [&](int t, int i) {
-    bool cache;
+  auto start_k = [&](int t, int i, auto ct) {
+    constexpr bool cache = decltype(ct)::value;
     int key0, nvalid;
-    tile_info(t, cache, key0, nvalid);
-    if (I8 && cache) {
+    tile_info(t, ct, key0, nvalid);
+    if constexpr (I8 && cache) {
+      unsigned char* Ks = kbuf(i);
 #pragma unroll
       for (int j = 0; j < C::NK8; ++j) {
-        const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
+        const int c = (j * NW + wave) * 64 + lane, row = c / (D / 16), cc = c % (D / 16);
         stk[j] = __builtin_amdgcn_raw_buffer_load_b128(rk_c, row * D + cc * 16, key0 * D, 0);
       }
-      if (tid < BC) sks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks_c, tid * 4, key0 * 4, 0));
+      if (wave == 0)
+#pragma unroll
+        for (int j = 0; j < BC / 64; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rks_c, (__attribute__((address_space(3))) void*)(Ks + C::KT_BYTES + j * 256),
+                                                   4, (j * 64 + lane) * 4, key0 * 4, 0, 0);
     } else {
       // each wave instruction fills 1 KB of LDS, lane l at byte 16*l; the lane
       // fetches the global chunk that the swizzled layout puts there
@@ -347,19 +362,20 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       }
     }
   };
-  auto start_v = [&](int t, int i) {
-    bool cache;
+  auto start_v = [&](int t, int i, auto ct) {
+    constexpr bool cache = decltype(ct)::value;
     int key0, nvalid;
-    tile_info(t, cache, key0, nvalid);
-    if (I8 && cache) {
+    tile_info(t, ct, key0, nvalid);
+    if constexpr (I8 && cache) {
 #pragma unroll
       for (int j = 0; j < C::NV8; ++j) {
-        const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
+        const int c = (j * NW + wave) * 64 + lane, d = c / (BC / 16), cc = c % (BC / 16);
         stv[j] = __builtin_amdgcn_raw_buffer_load_b128(rv_c, d * a.pitch_c + cc * 16, key0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          svs[j][e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs_c, (cc * 16 + 4 * e) * 4, key0 * 4, 0));
       }
+#pragma unroll
+      for (int j = 0; j < BC / 64; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs_c, (__attribute__((address_space(3))) void*)(vsc() + j * 256), 4,
+                                                 (j * 64 + lane) * 4, key0 * 4, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t rv = cache ? rv_c : rv_n;
       const int vstride = (cache ? a.pitch_c : a.pitch_cur) * 2;
@@ -374,41 +390,46 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   };
 
-  // ---- complete the staging of tile t's keys / values (INT8: convert + store);
-  // direct copies are waited for by wait_copies()
-  auto finish_k = [&](int t, int i) {
-    bool cache;
+  // ---- complete the staging of tile t's keys / values (INT8: convert + store),
+  // after wait_copies(): this wave's own loads and copies have landed
+  auto finish_k = [&](int t, int i, auto ct) {
+    constexpr bool cache = decltype(ct)::value;
     int key0, nvalid;
-    tile_info(t, cache, key0, nvalid);
-    if (I8 && cache) {
+    tile_info(t, ct, key0, nvalid);
+    if constexpr (I8 && cache) {
       unsigned char* Ks = kbuf(i);
 #pragma unroll
       for (int j = 0; j < C::NK8; ++j) {
-        const int c = tid + C::NT * j, row = c / (D / 16), cc = c % (D / 16);
+        const int c = (j * NW + wave) * 64 + lane, row = c / (D / 16), cc = c % (D / 16);
         u32x4 lo, hi;
         i8x16_to_bf16(stk[j], lo, hi);
         const int s = swz_k<D>(row);
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
+        __builtin_amdgcn_sched_barrier(0);   // one piece at a time: few live registers
       }
-      // the tile's key scales travel with its keys
-      if (tid < BC) reinterpret_cast<float*>(Ks + C::KT_BYTES)[tid] = sks;
     }
   };
-  auto finish_v = [&](int t, int i) {
-    bool cache;
+  auto finish_v = [&](int t, int i, auto ct) {
+    constexpr bool cache = decltype(ct)::value;
     int key0, nvalid;
-    tile_info(t, cache, key0, nvalid);
-    if (I8 && cache) {
+    tile_info(t, ct, key0, nvalid);
+    if constexpr (I8 && cache) {
       unsigned char* Vs = vbuf(i);
+      // a lane's chunks all cover keys 16*cc .. 16*cc+15
+      const int cc = lane % (BC / 16);
+      f32x4 sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = *reinterpret_cast<const f32x4*>(vsc() + (cc * 16 + 4 * e) * 4);
 #pragma unroll
       for (int j = 0; j < C::NV8; ++j) {
-        const int c = tid + C::NT * j, d = c / (BC / 16), cc = c % (BC / 16);
+        const int d = ((j * NW + wave) * 64 + lane) / (BC / 16);
         u32x4 lo, hi;
-        i8x16_dequant_bf16(stv[j], svs[j], lo, hi);
+        i8x16_dequant_bf16(stv[j], sc, lo, hi);
         const int s = swz_v<BC>(d);
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc) ^ s) * 16)) = lo;
         *reinterpret_cast<u32x4*>(Vs + d * BC * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -578,8 +599,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // PIPE: step j does the softmax and value MFMAs of tile j beside the logit
   // MFMAs and row max of tile j+1, while K(j+2) and V(j+1) are in flight.
   // Otherwise: tile by tile, the next tile's copies in flight during its MFMAs.
-  auto run_full = [&](int t0, int n, auto scaled_tag) {
+  auto run_full = [&](int t0, int n, auto ct) {
     if (n <= 0) return;
+    const std::bool_constant<I8 && decltype(ct)::value> scaled_tag;
     if constexpr (PIPE) {
       // Ping-pong: each tile is an MFMA phase H1(t) = [values of t-1, logits of
       // t] and a VALU phase H2(t) = [softmax of t]. The two wave groups (one wave
@@ -592,21 +614,21 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       const int grp = PP_GROUP(wave);
       auto vb = [](int s) { return VPF ? s % 3 : s & 1; };
       auto issue = [&](int s) {
-        if (s < n) start_k(t0 + s, s & 1);
+        if (s < n) start_k(t0 + s, s & 1, ct);
         const int sv = VPF ? s : s - 1;
-        if (sv >= 0 && sv < n) start_v(t0 + sv, vb(sv));
+        if (sv >= 0 && sv < n) start_v(t0 + sv, vb(sv), ct);
       };
       auto complete = [&](int s) {
-        if (s < n) finish_k(t0 + s, s & 1);
-        const int sv = VPF ? s : s - 1;
-        if (sv >= 0 && sv < n) finish_v(t0 + sv, vb(sv));
         wait_copies();
+        if (s < n) finish_k(t0 + s, s & 1, ct);
+        const int sv = VPF ? s : s - 1;
+        if (sv >= 0 && sv < n) finish_v(t0 + sv, vb(sv), ct);
       };
-      start_k(t0, 0);
-      if constexpr (VPF) start_v(t0, 0);
-      finish_k(t0, 0);
-      if constexpr (VPF) finish_v(t0, 0);
+      start_k(t0, 0, ct);
+      if constexpr (VPF) start_v(t0, 0, ct);
       wait_copies();
+      finish_k(t0, 0, ct);
+      if constexpr (VPF) finish_v(t0, 0, ct);
       __syncthreads();
       f32x4 sacc[QB][NKB];
       bf16x8 pf[QB][BC / 32];
@@ -641,18 +663,18 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       __syncthreads();
       if (grp == 0) __syncthreads();   // group A's idle last slot
     } else {
-      start_k(t0, 0);
-      start_v(t0, 0);
-      finish_k(t0, 0);
-      finish_v(t0, 0);
+      start_k(t0, 0, ct);
+      start_v(t0, 0, ct);
       wait_copies();
+      finish_k(t0, 0, ct);
+      finish_v(t0, 0, ct);
       __syncthreads();
       for (int j = 0; j < n; ++j) {
         const int i = j & 1;
         const bool more = j + 1 < n;
         if (more) {
-          start_k(t0 + j + 1, i ^ 1);
-          start_v(t0 + j + 1, i ^ 1);
+          start_k(t0 + j + 1, i ^ 1, ct);
+          start_v(t0 + j + 1, i ^ 1, ct);
         }
         f32x4 s[QB][NKB];
         logits(i, s, scaled_tag);
@@ -660,9 +682,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         probs(s, pf);
         values(i, pf, no_reads);
         if (more) {
-          finish_k(t0 + j + 1, i ^ 1);
-          finish_v(t0 + j + 1, i ^ 1);
           wait_copies();
+          finish_k(t0 + j + 1, i ^ 1, ct);
+          finish_v(t0 + j + 1, i ^ 1, ct);
         }
         __syncthreads();
       }
@@ -670,15 +692,15 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   };
 
   // ---- one partial tile (keys past nvalid masked), unpipelined
-  auto run_partial = [&](int t, auto scaled_tag) {
-    bool cache;
+  auto run_partial = [&](int t, auto ct) {
+    const std::bool_constant<I8 && decltype(ct)::value> scaled_tag;
     int key0, nvalid;
-    tile_info(t, cache, key0, nvalid);
-    start_k(t, 0);
-    start_v(t, 0);
-    finish_k(t, 0);
-    finish_v(t, 0);
+    tile_info(t, ct, key0, nvalid);
+    start_k(t, 0, ct);
+    start_v(t, 0, ct);
     wait_copies();
+    finish_k(t, 0, ct);
+    finish_v(t, 0, ct);
     __syncthreads();
     zero_tail(0, nvalid);
     __syncthreads();
@@ -716,13 +738,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     const int full_c = full_c_b, full_n = a.n_cur / BC;
     const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
     const int n_lo = max(t_begin, tiles_c_b), n_hi = min(t_end, tiles_c_b + full_n);
-    if (I8) run_full(c_lo, c_hi - c_lo, T_{});
-    else run_full(c_lo, c_hi - c_lo, F_{});
+    run_full(c_lo, c_hi - c_lo, T_{});
     run_full(n_lo, max(0, n_hi - n_lo), F_{});
-    if (full_c < tiles_c_b && t_begin <= full_c && full_c < t_end) {
-      if (I8) run_partial(full_c, T_{});
-      else run_partial(full_c, F_{});
-    }
+    if (full_c < tiles_c_b && t_begin <= full_c && full_c < t_end) run_partial(full_c, T_{});
     const int pn = tiles_c_b + full_n;
     if (pn < tiles_total_b && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
   }
@@ -815,8 +833,9 @@ struct Plan {
 
 // Tile shape per head dim and cache type: keys per tile, waves per block,
 // 16-query blocks per wave, ping-pong schedule, V prefetch across the barrier
-// (three V stages). INT8 tiles stage through registers, which leaves no room
-// for 128-key tiles in the ping-pong register budget.
+// (three V stages). INT8 tiles stage their codes through registers, which
+// leaves no room for 128-key tiles in the ping-pong register budget (two waves
+// per SIMD, 256 registers each).
 template <int D, bool I8> struct Shape;
 #ifndef NOMAS_ATTN_BC
 #define NOMAS_ATTN_BC 128

@@ -235,3 +235,40 @@ def test_rising_logits_raise_reference(D, int8, splits):
     # logits reach ~1.5e3 (natural units): fp32 rounding of the logit itself adds
     # a few ulp of that size on top of the probability-sum bound
     assert np.max(np.abs(g_lse - ref_lse)) <= LSE_TOL + 1e-3, np.max(np.abs(g_lse - ref_lse))
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_values_of_one_key_range(D, int8):
+    """Values nonzero in one key range at a time (a full cache tile, the partial
+    last cache tile, a full current tile, the partial last current tile), with
+    all other values zero: the output is then that range's share alone, so a
+    tile whose values are lost, misplaced or zeroed in LDS shows as a large
+    error, not one hidden under the tolerance. 6 frames of 240 cached rows =
+    1,440 (a partial last tile for both key-tile sizes), 480 + 40 current rows
+    (a partial last current tile)."""
+    H, tpf, frames, nv, nt = 2, 240, 6, 480, 40
+    n_cached, n_q = frames * tpf, nv + nt
+    kp = synth.normal_bf16((n_cached, H, D), 71, 0, 0, 3)
+    vp_all = synth.normal_bf16((n_cached, H, D), 71, 0, 0, 4)
+    q = synth.normal_bf16((n_q, H, D), 71, 0, 0, 0)
+    kc = synth.normal_bf16((n_q, H, D), 71, 0, 0, 1)
+    vc_all = synth.normal_bf16((n_q, H, D), 71, 0, 0, 2)
+    kpf = synth.bf16_bits_to_f64(kp)
+    if int8:
+        kpf = quant.dequantise(*quant.quantise(kpf))
+    x = [synth.bf16_bits_to_f64(t) for t in (q, kc)]
+    for part, lo, hi in (("cache", 128, 256), ("cache", 1408, 1440), ("current", 128, 256), ("current", 512, 520)):
+        vp = np.zeros_like(vp_all)
+        vc = np.zeros_like(vc_all)
+        (vp if part == "cache" else vc)[lo:hi] = (vp_all if part == "cache" else vc_all)[lo:hi]
+        say(f"attention: values of {part} rows [{lo}, {hi}) only, D={D} int8={int8}")
+        cache = nomas.KVCache(H, D, tpf, frames, int8)
+        cache.nomas_kvcache_append(dev_bf16(kp), dev_bf16(vp), frames)
+        out = nomas.nomas_segment_attention(dev_bf16(q), dev_bf16(kc), dev_bf16(vc), nv, nt, cache, n_splits=1)
+        torch.cuda.synchronize()
+        vpf = synth.bf16_bits_to_f64(vp)
+        if int8:
+            vpf = quant.dequantise(*quant.quantise(vpf))
+        ref, _ = attention.segment_attention(x[0], x[1], synth.bf16_bits_to_f64(vc), kpf, vpf, 1.0 / math.sqrt(D))
+        _check(host_f64(out), ref, f"values of {part} rows [{lo}, {hi}) only")

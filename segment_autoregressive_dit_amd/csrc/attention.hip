@@ -638,8 +638,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         __syncthreads();
       }
       for (int t = 0; t < n; ++t) {
-        // H1(t)
-        if (grp == 0) issue(t + 1);
+        // H1(t). The MFMA wave takes issue priority over the softmax wave on its
+        // SIMD, so each MFMA goes out as soon as the matrix core frees. Group A's
+        // copies for the next tile are split around the value MFMAs (keys first,
+        // values after), so neither batch of copy issues delays many MFMAs.
+        __builtin_amdgcn_s_setprio(1);
+        if (grp == 0 && t + 1 < n) start_k(t0 + t + 1, (t + 1) & 1, ct);
+        if (VPF && grp == 0 && t + 1 < n) start_v(t0 + t + 1, vb(t + 1), ct);
         bf16x8 k0[KH];   // first K fragments of tile t, landing during the value MFMAs
         if constexpr (VPF) {
           read_k0(t & 1, k0);
@@ -647,8 +652,10 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         } else {
           if (t >= 1) values(vb(t - 1), pf, [&]() { read_k0(t & 1, k0); });
           else read_k0(t & 1, k0);
+          if (grp == 0 && t < n) start_v(t0 + t, vb(t), ct);
         }
         logits_from(t & 1, k0, sacc, scaled_tag);
+        __builtin_amdgcn_s_setprio(0);
         if (grp == 1) complete(t + 1);
         __syncthreads();
         // H2(t)

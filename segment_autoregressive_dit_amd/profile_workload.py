@@ -16,6 +16,14 @@ Summarize rocprofv3 SQLite results (``*_results.db``) into short text files::
     python -m segment_autoregressive_dit_amd.profile_workload trace DB --out FILE.md --command "..."
     python -m segment_autoregressive_dit_amd.profile_workload traffic --fetch DB --write DB \\
         --copy-fetch DB --copy-write DB --copy-bytes N --kernel attn_kernel --out FILE.json --command "..."
+    python -m segment_autoregressive_dit_amd.profile_workload mfma DB --kernel attn_kernel \\
+        --algorithmic-flop F --out FILE.json --command "..."
+
+``traffic`` also reports the matched dispatches' average duration in the
+counter runs and the HBM rate it implies (counter runs serialise kernels, so the
+duration can read a little long). ``mfma`` reads a run of rocprofv3's derived
+counters ``MfmaUtil`` (MFMA busy cycles over active cycles of all SIMDs, %) and
+``MfmaFlopsBF16`` (bf16 MFMA operations x 512).
 """
 
 import argparse
@@ -126,6 +134,15 @@ def _counter_per_dispatch(db, counter, kernel_substr):
     return sum(vals) / len(vals), len(vals)
 
 
+def _dispatch_duration_ns(db, counter, kernel_substr):
+    con = sqlite3.connect(db)
+    cur = con.cursor()
+    rows = cur.execute("select dispatch_id, kernel_name, counter_name, duration from counters_collection").fetchall()
+    con.close()
+    per = {did: dur for did, kn, cn, dur in rows if cn == counter and kernel_substr in kn}
+    return sum(per.values()) / len(per) if per else None
+
+
 def cmd_traffic(a):
     fetch, nf = _counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
     write, nw = _counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
@@ -146,6 +163,37 @@ def cmd_traffic(a):
         "fetch_calibration": f_fac, "write_calibration": w_fac,
         "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
         "hbm_bytes_per_launch": fetch_b + write_b,
+        "source": a.source,
+        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "command": a.command,
+    }
+    dur = _dispatch_duration_ns(a.fetch, "FETCH_SIZE", a.kernel)
+    if dur:
+        out["duration_us_in_counter_run"] = dur / 1e3
+        out["hbm_gbps_counted"] = (fetch_b + write_b) / dur
+        out["hbm_frac_of_8tbps_counted"] = (fetch_b + write_b) / dur / 8000.0
+        if a.algorithmic_bytes:
+            out["algorithmic_bytes_per_launch"] = a.algorithmic_bytes
+            out["algorithmic_gbps"] = a.algorithmic_bytes / dur
+    with open(a.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def cmd_mfma(a):
+    util, nu = _counter_per_dispatch(a.db, "MfmaUtil", a.kernel)
+    mflop, nf = _counter_per_dispatch(a.db, "MfmaFlopsBF16", a.kernel)
+    dur = _dispatch_duration_ns(a.db, "MfmaUtil", a.kernel)
+    src = os.path.join(HERE, "csrc", a.source)
+    out = {
+        "kernel": a.kernel, "workload": a.workload, "dispatches": [nu, nf],
+        "mfma_util_pct": util,
+        "mfma_bf16_flop_per_launch": mflop,
+        "algorithmic_flop_per_launch": a.algorithmic_flop,
+        "mfma_flop_over_algorithmic": mflop / a.algorithmic_flop if a.algorithmic_flop else None,
+        "duration_us_in_counter_run": dur / 1e3 if dur else None,
+        "algorithmic_tflops_in_counter_run": a.algorithmic_flop / dur / 1e3 if dur and a.algorithmic_flop else None,
         "source": a.source,
         "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
         "command": a.command,
@@ -179,8 +227,17 @@ def main(argv=None):
     f.add_argument("--workload", default="layer_bf16")
     f.add_argument("--source", default="attention.hip")
     f.add_argument("--command", default="")
+    f.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    m = sub.add_parser("mfma")
+    m.add_argument("db")
+    m.add_argument("--out", required=True)
+    m.add_argument("--kernel", default="attn_kernel")
+    m.add_argument("--workload", default="layer_bf16")
+    m.add_argument("--source", default="attention.hip")
+    m.add_argument("--algorithmic-flop", type=float, default=0.0)
+    m.add_argument("--command", default="")
     a = p.parse_args(argv)
-    {"run": cmd_run, "trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
+    {"run": cmd_run, "trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -69,17 +69,18 @@ def _random_lists(H, nqb, nc, n_sel, seed):
     return lists
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("int8", [False, True])
-def test_sparse_attention_given_lists(int8, splits):
+def test_sparse_attention_given_lists(int8, splits, D):
     # 12x20 grid, 6 cached frames = 1,440 rows = 12 candidate blocks (the last of
     # 32 rows); 2-frame segment + 40 text = 520 queries = 3 query blocks
-    H, D, tpf, nv, nt = 2, 128, 240, 480, 40
+    H, tpf, nv, nt = 2, 240, 480, 40
     (q, k, v), cache, x, kp, vp = _setup(H, D, tpf, 6, nv, nt, int8, seed=int8)
     nc = sparse.n_candidates(kp.shape[0])
     assert nc == 12
     lists = _random_lists(H, 3, nc, 3, seed=10 + splits)
-    say(f"sparse attention: int8={int8} splits={splits}")
+    say(f"sparse attention: int8={int8} splits={splits} D={D}")
     lse = torch.empty(H * (nv + nt), dtype=torch.float32, device="cuda")
     out = nomas.nomas_segment_attention_sparse(q, k, v, nv, nt, cache, torch.from_numpy(lists).cuda(), lse=lse,
                                                n_splits=splits)
@@ -89,13 +90,14 @@ def test_sparse_attention_given_lists(int8, splits):
     assert np.max(np.abs(lse.cpu().numpy().reshape(H, -1) - ref_lse)) <= LSE_TOL
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("int8", [False, True])
-def test_all_blocks_equals_dense(int8):
-    H, D, tpf, nv, nt = 2, 128, 240, 480, 40
+def test_all_blocks_equals_dense(int8, D):
+    H, tpf, nv, nt = 2, 240, 480, 40
     (q, k, v), cache, _, kp, _ = _setup(H, D, tpf, 6, nv, nt, int8, seed=2)
     nc = sparse.n_candidates(kp.shape[0])
     lists = torch.arange(nc, dtype=torch.int32).repeat(H, 3, 1).cuda()
-    say(f"sparse all blocks vs dense: int8={int8}")
+    say(f"sparse all blocks vs dense: int8={int8} D={D}")
     a = nomas.nomas_segment_attention_sparse(q, k, v, nv, nt, cache, lists, n_splits=1)
     b = nomas.nomas_segment_attention(q, k, v, nv, nt, cache, n_splits=1)
     torch.cuda.synchronize()
@@ -112,12 +114,13 @@ def test_no_blocks_is_segment_only():
     _check(host_f64(out), ref, "no blocks")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("int8", [False, True])
-def test_selection_is_valid(int8):
-    H, D, tpf, nv, nt = 2, 128, 240, 480, 40
+def test_selection_is_valid(int8, D):
+    H, tpf, nv, nt = 2, 240, 480, 40
     (q, _, _), cache, x, kp, _ = _setup(H, D, tpf, 6, nv, nt, int8, seed=4)
     nc = sparse.n_candidates(kp.shape[0])
-    say(f"sparse select: int8={int8}")
+    say(f"sparse select: int8={int8} D={D}")
     for n_sel in (1, 3, nc):
         got = nomas.nomas_sparse_select(q, nv + nt, cache, n_sel).cpu().numpy()
         scores = sparse.block_scores(x[0], kp)

@@ -27,6 +27,11 @@ Also reported (outside the timed steps):
     same turns under the sparse policy (steps 1-2 dense, then candidate-block
     selection + attention to 25 % of the blocks) -> ``denoise_sparse_ms_per_step``
     (mean over the 8 steps of a turn, averaged over turns);
+  * the attention launch with the caches flushed between reps (512 MB written)
+    -> ``attention_cold_ms``; p10/p90 of the timed steps' attention launches;
+  * turn 12 of a full-history session (84,480 cached tokens), split-KV with
+    n_splits 1, 2, 4, 8 and auto -> ``long_history_ms``, ``long_history_tflops``
+    (auto);
   * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline``.
 Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
@@ -114,6 +119,8 @@ def layer_step_bench(args):
         flop=flop,
         attn_ms_mean=statistics.mean(attn_ms),
         attn_ms_median=statistics.median(attn_ms),
+        attn_ms_p10=statistics.quantiles(attn_ms, n=10)[0],
+        attn_ms_p90=statistics.quantiles(attn_ms, n=10)[-1],
         rope_ms_mean=statistics.mean(rope_ms),
         append_ms_mean=statistics.mean(app_ms),
         rope_bytes=2 * 2 * wl.n_video * H * D * 2,             # read + write Q and K video rows
@@ -122,6 +129,74 @@ def layer_step_bench(args):
     log(f"[bench] layer step: {res['ms_per_step']:.3f} ms/step, attention {res['attn_ms_mean']:.3f} ms "
         f"({flop / res['attn_ms_mean'] / 1e9:.1f} TFLOP/s)")
     return wl, res
+
+
+def attention_cold_bench(reps=20):
+    """The layer-shape attention launch with the caches flushed before each rep:
+    512 MB (twice the MALL) written between reps, so K/V come from HBM."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["layer_bf16"]
+    H, D = wl.n_heads, wl.head_dim
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, False)
+    kb, vb = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    out = torch.empty_like(q)
+    ws = nomas.workspace_for(cache, wl.n_video, wl.n_text)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
+    ms = []
+    for i in range(reps):
+        flush.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = statistics.median(ms)
+    log(f"[bench] attention, caches flushed: {med:.3f} ms ({wl.attention_flop() / med / 1e9:.1f} TFLOP/s)")
+    return dict(attention_cold_ms=round(med, 4), attention_cold_tflops=round(wl.attention_flop() / med / 1e9, 1))
+
+
+def long_history_bench(reps=10):
+    """Turn 12 of a session with full history: 84,480 cached tokens (88 frames) +
+    7,936 current rows, 16x128 heads, bf16; split-KV with n_splits in
+    {1, 2, 4, 8, auto}."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["long_bf16"]
+    H, D = wl.n_heads, wl.head_dim
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, False)
+    kb, vb = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    del kb, vb
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    out = torch.empty_like(q)
+    flop = wl.attention_flop()
+    res = {}
+    for splits in (1, 2, 4, 8, 0):
+        ws = nomas.workspace_for(cache, wl.n_video, wl.n_text, splits)
+        for _ in range(2):
+            nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, n_splits=splits, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, n_splits=splits, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[splits] = ms
+        del ws
+    best = min(res, key=res.get)
+    log("[bench] long history: " + ", ".join(f"splits {s or 'auto'} {m:.3f} ms" for s, m in res.items()))
+    return dict(long_history_ms={str(s or "auto"): round(m, 4) for s, m in res.items()},
+                long_history_tflops=round(flop / res[0] / 1e9, 1),
+                long_history_best_tflops=round(flop / res[best] / 1e9, 1))
 
 
 def denoise_bench(n_turns=3):
@@ -407,7 +482,11 @@ def main():
         rope_gbps=round(r["rope_bytes"] / (r["rope_ms_mean"] * 1e-3) / 1e9, 1),
         append_us=round(r["append_ms_mean"] * 1e3, 2),
         append_gbps=round(r["append_bytes"] / (r["append_ms_mean"] * 1e-3) / 1e9, 1),
+        attention_ms_p10=round(r["attn_ms_p10"], 4),
+        attention_ms_p90=round(r["attn_ms_p90"], 4),
     )
+    extra.update(attention_cold_bench())
+    extra.update(long_history_bench())
     if not args.no_denoise:
         d = denoise_bench()
         extra.update(denoise_sparse_ms_per_step=round(d["denoise_sparse_ms_per_step"], 3),

@@ -60,8 +60,9 @@ def test_append_bit_exact_against_ring_model(case, int8):
 
 
 def _crafted_frame(tpf, H, D, seed):
-    """Vectors that stress the quantiser: zeros, x = m/2 ties, subnormal scales,
-    huge values, a single non-zero, negative maxima."""
+    """Vectors that stress the quantiser: zeros, x = m/2 ties, ties next to even
+    codes (absmax 127: the scale is 1 and 2.5 -> 2, 62.5 -> 62), subnormal
+    scales, huge values, a single non-zero, negative maxima."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((tpf, H, D)).astype(np.float32)
     from_bits = synth.bf16_bits_to_f64
@@ -77,6 +78,8 @@ def _crafted_frame(tpf, H, D, seed):
         x[6, h] = 0.0
         x[6, h, 5] = -3.0
         x[7, h] = -np.abs(x[7, h])
+        x[8, h] = 0.0
+        x[8, h, :10] = [127.0, 0.5, 1.5, 2.5, 3.5, 62.5, 63.5, -0.5, -2.5, -62.5]
     return synth._round_bf16_bits(x)
 
 

@@ -38,6 +38,18 @@ def test_special_cases():                              # Q2
     assert q.dtype == np.int8 and s.dtype == np.float32
 
 
+def test_ties_round_to_even():                         # Q2: the tie rule of round-half-even
+    # absmax 127 makes the scale exactly 1, so each code is the rounded value
+    # itself; .5 ties between an even and an odd code go to the even one
+    vals = [127.0, 0.5, 1.5, 2.5, 3.5, 62.5, 63.5, -0.5, -2.5, -62.5, 2.25, -2.75]
+    want = [127, 0, 2, 2, 4, 62, 64, 0, -2, -62, 2, -3]
+    x = np.zeros((1, 64))
+    x[0, :len(vals)] = vals
+    q, s = quant.quantise(x)
+    assert float(s[0]) == 1.0
+    assert list(q[0, :len(vals)]) == want
+
+
 def test_every_code_is_exact_in_bf16():                # Q4
     codes = np.arange(-127, 128, dtype=np.float64)
     assert np.array_equal(formats.to_bf16(codes), codes)

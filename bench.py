@@ -32,7 +32,9 @@ Also reported (outside the timed steps):
   * turn 12 of a full-history session (84,480 cached tokens), split-KV with
     n_splits 1, 2, 4, 8 and auto -> ``long_history_ms``, ``long_history_tflops``
     (auto);
-  * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline``.
+  * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline`` (all the
+    BLAS threads), and on one thread over a sample cut by the thread count
+    -> ``cpu_baseline.one_thread``.
 Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
 
@@ -441,9 +443,24 @@ def cpu_baseline(rows_per_head):
     dt = time.perf_counter() - t0
     flop = 4 * len(rows) * wl.n_k * wl.head_dim * wl.n_heads
     log(f"[bench] cpu oracle: {len(rows)} rows x {wl.n_heads} heads in {dt:.2f} s")
-    return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"{len(rows)} of {wl.n_q} query rows per head, all {wl.n_heads} heads, all {wl.n_k} keys "
-                       f"({flop / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy)")
+    out = dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+               sample=f"{len(rows)} of {wl.n_q} query rows per head, all {wl.n_heads} heads, all {wl.n_k} keys "
+                      f"({flop / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy)")
+    # the same oracle on one thread, on a sample cut by the thread count
+    try:
+        from threadpoolctl import threadpool_limits
+        rows1 = rows[::max(1, threads)]
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            attention.segment_attention(q[rows1], k, v, kp, vp, 1.0 / math.sqrt(wl.head_dim))
+            dt1 = time.perf_counter() - t0
+        flop1 = 4 * len(rows1) * wl.n_k * wl.head_dim * wl.n_heads
+        log(f"[bench] cpu oracle, 1 thread: {len(rows1)} rows x {wl.n_heads} heads in {dt1:.2f} s")
+        out["one_thread"] = dict(value=flop1 / dt1 / 1e12, unit="TFLOP/s", cores=1,
+                                 sample=f"{len(rows1)} query rows per head ({flop1 / 1e9:.1f} GFLOP in {dt1:.1f} s)")
+    except Exception as e:   # threadpoolctl missing: report the all-core figure only
+        log(f"[bench] cpu oracle, 1 thread: not measured ({e})")
+    return out
 
 
 def traffic_per_launch():

@@ -1,0 +1,121 @@
+"""Seeded random small shapes through the cached, block-causal and sparse
+attention calls, against the fp64 oracle: 1-3 heads, head dims 64 and 128,
+tokens per frame from 1 to 60 (odd ones included), empty to wrapped caches built
+by several appends, text-only and video-only segments, bf16 and INT8 caches,
+split counts 0-5. Full rows, the same tolerance as the other attention tests
+(max|diff| <= 1e-2 max|ref|, mean|diff| <= 1e-3). Every case is named before its
+GPU step."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, quant, sparse
+from oracle.ring import RingModel
+from segment_autoregressive_dit_amd import nomas, synth
+
+import test_gpu_block_causal as BC
+from _gpu_util import dev_bf16, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(got, ref, what):
+    diff = np.abs(got - ref)
+    mx, mean, lim = diff.max(), diff.mean(), 1e-2 * np.abs(ref).max()
+    assert mx <= lim and mean <= 1e-3, f"{what}: max|diff| {mx:.3e} (limit {lim:.3e}), mean {mean:.3e}"
+
+
+def _cached_case(i):
+    r = np.random.default_rng([2026, i])
+    H = int(r.choice([1, 2, 3]))
+    D = int(r.choice([64, 128]))
+    gh, gw = int(r.integers(1, 13)), int(r.integers(1, 21))
+    cap = int(r.integers(1, 6))
+    appends = [int(r.integers(1, cap + 3)) for _ in range(int(r.integers(0, 4)))]
+    F = int(r.integers(0, 4))
+    T = int(r.integers(0, 301))
+    if F == 0 and T == 0:
+        T = 1
+    return dict(H=H, D=D, gh=gh, gw=gw, cap=cap, appends=appends, F=F, T=T, int8=bool(r.integers(0, 2)),
+                splits=int(r.choice([0, 1, 2, 3, 5])))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_cached_attention_random_shapes(i):
+    c = _cached_case(i)
+    H, D, tpf = c["H"], c["D"], c["gh"] * c["gw"]
+    say(f"fuzz cached {i}: {c}")
+    cache = nomas.KVCache(H, D, tpf, c["cap"], c["int8"])
+    ring = RingModel(c["cap"])
+    for a, n in enumerate(c["appends"]):
+        kb = synth.normal_bf16((n * tpf, H, D), 90 + i, a, 0, 3)
+        vb = synth.normal_bf16((n * tpf, H, D), 90 + i, a, 0, 4)
+        cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), n)
+        ring.append([(kb[f * tpf:(f + 1) * tpf], vb[f * tpf:(f + 1) * tpf]) for f in range(n)])
+    nv, nt = c["F"] * tpf, c["T"]
+    q, k, v = (synth.normal_bf16((nv + nt, H, D), 90 + i, 9, 0, t) for t in range(3))
+    lse = torch.empty(H * (nv + nt), dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), nv, nt, cache, lse=lse,
+                                        n_splits=c["splits"])
+    torch.cuda.synchronize()
+    frames = ring.retained()
+    kp = vp = None
+    if frames:
+        kp = np.concatenate([synth.bf16_bits_to_f64(p[0]) for _, p in frames], 0)
+        vp = np.concatenate([synth.bf16_bits_to_f64(p[1]) for _, p in frames], 0)
+        if c["int8"]:
+            kp, vp = quant.dequantise(*quant.quantise(kp)), quant.dequantise(*quant.quantise(vp))
+    x = [synth.bf16_bits_to_f64(t) for t in (q, k, v)]
+    ref, ref_lse = attention.segment_attention(x[0], x[1], x[2], kp, vp, 1.0 / math.sqrt(D))
+    _check(host_f64(out), ref, f"case {i}")
+    assert np.max(np.abs(lse.cpu().numpy().reshape(H, -1) - ref_lse)) <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_block_causal_random_sessions(i):
+    r = np.random.default_rng([2027, i])
+    H, D = int(r.choice([1, 2, 3])), int(r.choice([64, 128]))
+    tpf = int(r.integers(1, 41))
+    segs, t = [], 0
+    for _ in range(int(r.integers(1, 5))):
+        F, T = int(r.integers(0, 4)), int(r.integers(0, 30))
+        if F == 0 and T == 0:
+            T = 1
+        segs.append((F * tpf, T, t))
+        t += F
+    window = [None, 0, 1, 2, 3][int(r.integers(0, 5))]
+    BC._run(segs, tpf, window, H, D, seed=200 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_sparse_attention_random_lists(i):
+    r = np.random.default_rng([2028, i])
+    H, D = int(r.choice([1, 2])), int(r.choice([64, 128]))
+    tpf = int(r.integers(20, 61))
+    frames = int(r.integers(1, 9))
+    int8 = bool(r.integers(0, 2))
+    nv, nt = int(r.integers(0, 3)) * tpf, int(r.integers(1, 300))
+    n_cached, n_q = frames * tpf, nv + nt
+    nc = sparse.n_candidates(n_cached)
+    nqb = (n_q + sparse.QUERY_BLOCK - 1) // sparse.QUERY_BLOCK
+    n_sel = int(r.integers(0, nc + 1))
+    lists = np.stack([np.stack([np.sort(r.choice(nc, n_sel, replace=False)) for _ in range(nqb)])
+                      for _ in range(H)]).astype(np.int32).reshape(H, nqb, n_sel)
+    say(f"fuzz sparse {i}: H={H} D={D} tpf={tpf} frames={frames} int8={int8} nv={nv} nt={nt} n_sel={n_sel}")
+    kp_b = synth.normal_bf16((n_cached, H, D), 300 + i, 0, 0, 3)
+    vp_b = synth.normal_bf16((n_cached, H, D), 300 + i, 0, 0, 4)
+    cache = nomas.KVCache(H, D, tpf, frames, int8)
+    cache.nomas_kvcache_append(dev_bf16(kp_b), dev_bf16(vp_b), frames)
+    q, k, v = (synth.normal_bf16((n_q, H, D), 300 + i, 1, 0, t) for t in range(3))
+    out = nomas.nomas_segment_attention_sparse(dev_bf16(q), dev_bf16(k), dev_bf16(v), nv, nt, cache,
+                                               torch.from_numpy(lists).cuda(), n_splits=int(r.choice([0, 1, 3])))
+    torch.cuda.synchronize()
+    kp, vp = synth.bf16_bits_to_f64(kp_b), synth.bf16_bits_to_f64(vp_b)
+    if int8:
+        kp, vp = quant.dequantise(*quant.quantise(kp)), quant.dequantise(*quant.quantise(vp))
+    x = [synth.bf16_bits_to_f64(t) for t in (q, k, v)]
+    ref, _ = sparse.sparse_segment_attention(x[0], x[1], x[2], kp, vp, lists, 1.0 / math.sqrt(D))
+    _check(host_f64(out), ref, f"sparse case {i}")

@@ -395,8 +395,11 @@ def nomas_block_causal_attention(q, k, v, segments, tokens_per_frame, window_fra
 
 def nomas_rope3d_table(head_dim, t0, n_frames, grid_h, grid_w, band, theta=10000.0, inverse=False, table=None,
                        stream=None):
-    """(cos, sin) table [n_frames*grid_h*grid_w, head_dim/2, 2] float32 of a segment's video rows."""
+    """(cos, sin) table [n_frames*grid_h*grid_w, head_dim/2, 2] float32 of a segment's video rows;
+    None for a segment without video rows (nothing to rotate: pass rope_table=None)."""
     n = n_frames * grid_h * grid_w
+    if n == 0:
+        return None
     if table is None:
         table = torch.empty((n, head_dim // 2, 2), dtype=torch.float32, device="cuda")
     if table.dtype != torch.float32 or not table.is_cuda or not table.is_contiguous() or table.numel() < n * head_dim:

@@ -119,3 +119,17 @@ def test_sparse_attention_random_lists(i):
     x = [synth.bf16_bits_to_f64(t) for t in (q, k, v)]
     ref, _ = sparse.sparse_segment_attention(x[0], x[1], x[2], kp, vp, lists, 1.0 / math.sqrt(D))
     _check(host_f64(out), ref, f"sparse case {i}")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_qkv_projection_random_shapes(i):
+    import test_gpu_qkv as QK
+    r = np.random.default_rng([2029, i])
+    H, D = int(r.integers(1, 7)), int(r.choice([64, 128]))
+    hidden = int(r.choice([64, 128, 192, 320, 1024]))
+    F, gh, gw = int(r.integers(0, 3)), int(r.integers(1, 9)), int(r.integers(1, 13))
+    T = int(r.integers(0, 200))
+    if F * gh * gw + T == 0:
+        T = 1
+    band = (D // 4, 3 * D // 8, 3 * D // 8)
+    QK._run(H, D, hidden, F, gh, gw, T, int(r.integers(0, 40)), band, seed=400 + i)

@@ -133,3 +133,54 @@ def test_qkv_projection_random_shapes(i):
         T = 1
     band = (D // 4, 3 * D // 8, 3 * D // 8)
     QK._run(H, D, hidden, F, gh, gw, T, int(r.integers(0, 40)), band, seed=400 + i)
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_append_random_sequences_bit_exact(i):
+    import test_gpu_kvcache as KV
+    r = np.random.default_rng([2030, i])
+    H, D = int(r.integers(1, 5)), int(r.choice([64, 128]))
+    tpf = int(r.integers(1, 301))
+    cap = int(r.integers(1, 13))
+    int8 = bool(r.integers(0, 2))
+    sizes = [int(r.integers(1, 2 * cap + 2)) for _ in range(int(r.integers(1, 6)))]
+    say(f"fuzz append {i}: H={H} D={D} tpf={tpf} cap={cap} int8={int8} sizes={sizes}")
+    cache = nomas.KVCache(H, D, tpf, cap, int8)
+    ring = RingModel(cap)
+    for a, n in enumerate(sizes):
+        kb = synth.normal_bf16((n * tpf, H, D), 500 + i, a, 0, 3)
+        vb = synth.normal_bf16((n * tpf, H, D), 500 + i, a, 0, 4)
+        cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), n)
+        ring.append([(kb[f * tpf:(f + 1) * tpf], vb[f * tpf:(f + 1) * tpf]) for f in range(n)])
+        KV._check_cache(cache, ring, tpf, int8)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_cached_attention_medium_shapes_sampled_rows(i):
+    # thousands of cached keys, many tiles per block, several query tiles: the
+    # ping-pong loop and the split bounds at sizes between the unit tests and
+    # the full layer
+    r = np.random.default_rng([2031, i])
+    H, D = int(r.integers(1, 5)), int(r.choice([64, 128]))
+    gh, gw = int(r.integers(4, 25)), int(r.integers(4, 41))
+    tpf = gh * gw
+    cap = int(r.integers(2, 9))
+    F, T = int(r.integers(1, 4)), int(r.integers(0, 257))
+    int8 = bool(r.integers(0, 2))
+    splits = int(r.choice([0, 1, 2, 4, 7]))
+    say(f"fuzz medium {i}: H={H} D={D} tpf={tpf} cap={cap} F={F} T={T} int8={int8} splits={splits}")
+    cache = nomas.KVCache(H, D, tpf, cap, int8)
+    kb = synth.normal_bf16((cap * tpf, H, D), 600 + i, 0, 0, 3)
+    vb = synth.normal_bf16((cap * tpf, H, D), 600 + i, 0, 0, 4)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), cap)
+    nv, nt = F * tpf, T
+    q, k, v = (synth.normal_bf16((nv + nt, H, D), 600 + i, 1, 0, t) for t in range(3))
+    out = nomas.nomas_segment_attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), nv, nt, cache, n_splits=splits)
+    torch.cuda.synchronize()
+    kp, vp = synth.bf16_bits_to_f64(kb), synth.bf16_bits_to_f64(vb)
+    if int8:
+        kp, vp = quant.dequantise(*quant.quantise(kp)), quant.dequantise(*quant.quantise(vp))
+    rows = np.unique(np.r_[0, nv + nt - 1, max(0, nv - 1), min(nv, nv + nt - 1), r.integers(0, nv + nt, 40)])
+    x = [synth.bf16_bits_to_f64(t) for t in (q, k, v)]
+    ref, _ = attention.segment_attention(x[0][rows], x[1], x[2], kp, vp, 1.0 / math.sqrt(D))
+    _check(host_f64(out)[rows], ref, f"medium case {i}")

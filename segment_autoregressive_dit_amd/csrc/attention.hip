@@ -11,18 +11,24 @@
 //  * One block = NW waves = NW*QB*16 queries of one head and one key split.
 //    Each wave owns QB blocks of 16 queries; their Q fragments stay in VGPRs.
 //  * Logits are formed transposed, S^T = K Q^T, so a lane holds one query
-//    (lane % 16) and 4 keys per MFMA: row max / row sum need only two
-//    cross-lane steps (lanes 16 and 32 apart) per key tile.
+//    (lane % 16) and 4 keys per MFMA: a row max needs only two cross-lane steps
+//    (lanes 16 and 32 apart), and the row sums come from an MFMA against an
+//    all-ones operand.
 //  * The 32 keys of a group are fed to the two S^T MFMAs in a permuted row
 //    order so that lane group G ends up holding keys 8G..8G+7 in register
 //    order; that is exactly the B operand (P^T) layout of the value MFMA
 //    O^T += V^T P^T, so P never goes through LDS.
 //  * V^T operand rows are contiguous key runs: the cache stores V transposed and
 //    the current segment's V is transposed once into the workspace.
-//  * K and V^T tiles of BC keys are double-buffered in LDS (one barrier per
-//    tile), with the 16-byte chunk index XOR-swizzled by the row so that the
-//    strided 128-bit operand reads are bank-conflict free. The next tile's
-//    global loads are issued before the current tile's MFMAs.
+//  * K and V^T tiles of BC keys are double-buffered in LDS (INT8: three V^T
+//    stages), with the 16-byte chunk index XOR-swizzled by the row so that the
+//    strided 128-bit operand reads are bank-conflict free. bf16 tiles are copied
+//    global -> LDS by the load unit (buffer_load ... lds).
+//  * Head dim 128 runs a ping-pong schedule: the block's 8 waves form two
+//    groups, one wave of each on every SIMD, one barrier apart, so that on every
+//    SIMD one wave issues MFMAs (values of tile t-1, logits of tile t, at issue
+//    priority 1) while the other runs the softmax of its tile. Head dim 64 runs
+//    two 4-wave blocks per CU, tile by tile.
 //  * Online softmax in the log2 domain with a fixed reference max per query that
 //    is only raised when a tile's max exceeds it by more than kTau (probabilities
 //    stay <= 2^kTau, exact in fp32 and bf16 range), so the O rescale is rare.

@@ -204,8 +204,10 @@ int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_text, int64_t 
  * Block-causal segment attention of the current segment.
  * Queries: the n_q = n_video + n_text rows of q, video rows first then text.
  * Keys/values: the retained cache tokens (rows [0, valid_frames*tpf) of each
- * head of `*c`; INT8 entries enter as code*scale, applied in float32 per key
- * after an exact int8->bf16 conversion) followed by all n_q rows of k_cur/v_cur.
+ * head of `*c`) followed by all n_q rows of k_cur/v_cur. INT8 cache entries enter
+ * as code*scale: a key's codes convert to bf16 exactly and its scale multiplies
+ * the float32 logit; a value's code*scale is formed in float32 and rounded once
+ * to bf16.
  * Every query sees every such key: bidirectional inside the segment, and
  * earlier segments only through the cache (causal across segments).
  * out[r, h, :] = sum_j softmax_j(softmax_scale * <q[r,h,:], key_j>) value_j

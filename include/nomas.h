@@ -106,7 +106,10 @@ size_t nomas_kvcache_bytes(int32_t n_heads, int32_t head_dim, int32_t tokens_per
 
 /* Fill `*c` (host) for caller-allocated device buffers of the sizes above, with
  * frames_written = 0. Scales must be NULL for BF16 and non-NULL for INT8.
- * Buffer contents need no initialisation. */
+ * Buffer contents need no initialisation. One head's K (or V) slice,
+ * token_pitch * head_dim * element bytes, must stay below 2 GiB (the kernels
+ * address it with 32-bit byte offsets): NOMAS_E_INVALID otherwise, also from
+ * every later call handed a descriptor edited past that limit. */
 int32_t nomas_kvcache_init(nomas_kvcache* c, int32_t n_heads, int32_t head_dim,
                            int32_t tokens_per_frame, int32_t capacity_frames, int32_t kv_dtype,
                            void* k, void* v, float* k_scale, float* v_scale);
@@ -223,7 +226,8 @@ int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_text, int64_t 
  * c: (host) descriptor; its n_heads and head_dim are those of q, k_cur, v_cur, out.
  * softmax_scale > 0 (1/sqrt(head_dim) is the model's). workspace: (device),
  * 256-byte aligned, >= nomas_segment_attention_workspace_bytes(...).
- * n_video + n_text >= 1.
+ * n_video + n_text >= 1, and (n_video + n_text) * ld_qkv * 2 bytes below 2 GiB
+ * (32-bit byte ranges in the kernels): NOMAS_E_INVALID otherwise.
  */
 int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
                                 int64_t ld_qkv, int32_t n_video, int32_t n_text,
@@ -348,6 +352,7 @@ size_t nomas_block_causal_attention_workspace_bytes(const nomas_segment* segs, i
  * tokens_per_frame, n_text >= 0, n_video + n_text >= 1, t0 >= 0.
  * q, k, v: (device) bf16 [n_rows][ld_qkv]; out: (device) bf16 [n_rows][ld_out];
  * lse: (device) float32 [n_heads][n_rows] or NULL. head_dim 64 or 128.
+ * n_rows * ld_qkv * 2 bytes below 2 GiB (NOMAS_E_INVALID otherwise).
  * workspace: (device), 256-byte aligned, >= the bytes above. Arithmetic as in
  * nomas_segment_attention (bf16 MFMA products, float32 accumulation and softmax;
  * bitwise reproducible run to run).

@@ -958,6 +958,10 @@ static int32_t segment_attention_impl(const uint16_t* q, const uint16_t* k_cur, 
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(NOMAS_E_INVALID, "segment_attention: softmax_scale must be finite and > 0");
   if (n_splits < 0) return fail(NOMAS_E_INVALID, "segment_attention: n_splits must be >= 0");
+  // 32-bit byte ranges of the kernels' loads of the current rows and of V^T
+  if (((int64_t)n_video + n_text) * ld_qkv * 2 > INT32_MAX ||
+      (int64_t)D * round_up((int64_t)n_video + n_text, kTokenAlign) * 2 > INT32_MAX)
+    return fail(NOMAS_E_INVALID, "segment_attention: (n_video + n_text) * ld_qkv * 2 bytes must stay below 2 GiB");
   const int64_t n_cached = nomas_kvcache_valid_frames(c) * c->tokens_per_frame;
   const int64_t n_cand = (n_cached + kSpKeyBlock - 1) / kSpKeyBlock;
   if (sparse) {
@@ -1137,6 +1141,8 @@ extern "C" int32_t nomas_block_causal_attention(const uint16_t* q, const uint16_
     return fail(NOMAS_E_INVALID, "%s: ld_qkv and ld_out must be >= n_heads*head_dim and multiples of 8", who);
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(NOMAS_E_INVALID, "%s: softmax_scale must be finite and > 0", who);
+  if ((int64_t)p.n_rows * ld_qkv * 2 > INT32_MAX || (int64_t)D * p.pitch * 2 > INT32_MAX)
+    return fail(NOMAS_E_INVALID, "%s: rows * ld_qkv * 2 bytes must stay below 2 GiB", who);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(NOMAS_E_WORKSPACE, "%s: workspace must be non-NULL and 256-byte aligned", who);
   if (workspace_bytes < p.bytes)

@@ -173,6 +173,8 @@ int32_t validate_cache(const nomas_kvcache* c, const char* who) {
     return fail(NOMAS_E_INVALID, "%s: cache descriptor is not initialised (use nomas_kvcache_init)", who);
   if (c->token_pitch != nomas_kvcache_token_pitch(c->tokens_per_frame, c->capacity_frames))
     return fail(NOMAS_E_INVALID, "%s: cache token_pitch does not match its sizes", who);
+  if ((int64_t)c->token_pitch * c->head_dim * (c->kv_dtype == NOMAS_KV_INT8 ? 1 : 2) > INT32_MAX)
+    return fail(NOMAS_E_INVALID, "%s: one head's cache slice must stay below 2 GiB", who);
   if (!c->k || !c->v || !aligned16(c->k) || !aligned16(c->v))
     return fail(NOMAS_E_INVALID, "%s: cache buffers must be non-NULL and 16-byte aligned", who);
   if (c->kv_dtype == NOMAS_KV_INT8 && (!c->k_scale || !c->v_scale))

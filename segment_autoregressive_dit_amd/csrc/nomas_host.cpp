@@ -78,6 +78,9 @@ int32_t nomas_kvcache_init(nomas_kvcache* c, int32_t n_heads, int32_t head_dim, 
   if (pitch < 0) return fail(NOMAS_E_INVALID, "kvcache_init: capacity too large");
   if ((int64_t)n_heads * head_dim * pitch > ((int64_t)1 << 40))
     return fail(NOMAS_E_INVALID, "kvcache_init: cache larger than 1 TiB");
+  // the kernels address one head's K or V slice with 32-bit byte offsets
+  if (pitch * head_dim * (kv_dtype == NOMAS_KV_INT8 ? 1 : 2) > INT32_MAX)
+    return fail(NOMAS_E_INVALID, "kvcache_init: one head's cache slice (token_pitch*head_dim*element size) must stay below 2 GiB");
   if (!k || !v) return fail(NOMAS_E_INVALID, "kvcache_init: k and v buffers must be non-NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(NOMAS_E_INVALID, "kvcache_init: k and v must be 16-byte aligned");
   if (kv_dtype == NOMAS_KV_INT8) {

@@ -76,6 +76,33 @@ def test_kvcache_init_validation():
     assert L.nomas_kvcache_init(None, 2, 64, 24, 4, 0, f, f, None, None) == nomas.NOMAS_E_INVALID
 
 
+def test_per_head_slice_limit():
+    """The kernels address one head's K or V slice with 32-bit byte offsets, so a
+    cache whose per-head slice reaches 2 GiB is refused at init and by every call
+    that takes the descriptor (rather than wrapping on the GPU)."""
+    L = nomas.lib()
+    f = ctypes.c_void_p(1 << 20)
+    s = ctypes.c_void_p(1 << 21)
+    d = nomas.KVCacheDesc()
+    # bf16, head dim 128: token_pitch 8,387,584 -> 2,147,221,504 bytes per head (fits)
+    assert L.nomas_kvcache_init(ctypes.byref(d), 1, 128, 1024, 8191, 0, f, f, None, None) == 0
+    # token_pitch 8,389,632 -> 2,147,745,792 bytes: one past the limit
+    assert L.nomas_kvcache_init(ctypes.byref(d), 1, 128, 1024, 8193, 0, f, f, None, None) == nomas.NOMAS_E_INVALID
+    assert b"2 GiB" in L.nomas_last_error()
+    # INT8 codes are one byte: twice the tokens fit
+    assert L.nomas_kvcache_init(ctypes.byref(d), 1, 128, 1024, 16383, 1, f, f, s, s) == 0
+    assert L.nomas_kvcache_init(ctypes.byref(d), 1, 128, 1024, 16385, 1, f, f, s, s) == nomas.NOMAS_E_INVALID
+    # a descriptor edited past the limit is refused by the calls that read it
+    L2, d2, rc = _desc(dtype=0)
+    assert rc == 0
+    d2.tokens_per_frame, d2.capacity_frames = 1024, 16385
+    d2.token_pitch = L.nomas_kvcache_token_pitch(1024, 16385)
+    p = ctypes.c_void_p(1 << 24)
+    assert L.nomas_kvcache_append(ctypes.byref(d2), p, p, 128, 1, None) == nomas.NOMAS_E_INVALID
+    assert b"2 GiB" in L.nomas_last_error()
+    assert d2.frames_written == 0
+
+
 def test_append_rejects_before_launch_and_keeps_descriptor():
     L, d, _ = _desc()
     p = ctypes.c_void_p(1 << 24)
@@ -130,6 +157,10 @@ def test_attention_rejects_before_launch():
     assert call(ws=ctypes.c_void_p((1 << 26) + 16)) == nomas.NOMAS_E_WORKSPACE
     assert call(wsb=need - 1) == nomas.NOMAS_E_WORKSPACE
     assert b"workspace" in L.nomas_last_error()
+    # 64 rows at a row stride of 2**24 elements: 2 GiB of current-segment bytes,
+    # past the kernels' 32-bit byte ranges
+    assert call(ld=1 << 24, ldo=1 << 24) == nomas.NOMAS_E_INVALID
+    assert b"2 GiB" in L.nomas_last_error()
 
 
 def test_workspace_and_split_planning():
@@ -181,6 +212,8 @@ def test_block_causal_rejects_before_launch():
     assert call(wsb=need - 1) == nomas.NOMAS_E_WORKSPACE
     assert call(ws=None) == nomas.NOMAS_E_WORKSPACE
     assert b"workspace" in L.nomas_last_error()
+    assert call(ld=1 << 24, ldo=1 << 24) == nomas.NOMAS_E_INVALID     # 128 rows x 2**24 x 2 bytes
+    assert b"2 GiB" in L.nomas_last_error()
 
 
 def test_sparse_rejects_before_launch():

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   float m_ref[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_ref[qb] = -INFINITY;
+    m_ref[qb] = 0.f;
     lacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -522,45 +522,59 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
           for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
   };
 
-  // raise the reference max of query block qb to cover tile max mt
-  auto raise_ref = [&](int qb, float mt) {
-    const float mn = fmaxf(m_ref[qb], mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - mn);
-    lacc[qb] *= alpha;
+  // raise the reference max of query block qb by up (log2 units); the first
+  // tile of a block sets it outright (O and the sums are still zero)
+  bool fresh = true;
+  auto raise_ref = [&](int qb, float up) {
+    if (!fresh) {
+      const float alpha = __builtin_amdgcn_exp2f(-up);
+      lacc[qb] *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[qb][db] *= alpha;
-    m_ref[qb] = mn;
+      for (int db = 0; db < D / 16; ++db) o[qb][db] *= alpha;
+    }
+    m_ref[qb] += up;
   };
 
   // P = exp2(c2*s - m_ref) as bf16 MFMA operands, against a running reference
-  // max per query that is raised -- O and the sums rescaled -- only when a logit
-  // of the tile exceeds it by more than kTau (always on the first tile, where it
-  // is -inf). Every probability is thus at most 2^kTau, and raises are rare
-  // after the first tile. Each lane tests the maximum of its own logits; a raise
-  // takes the exact tile max over the query's four lanes.
-  auto probs = [&](const f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32]) {
+  // max per query. The exponents t = c2*s - m_ref are formed in place first and
+  // each lane tests the maximum of its own (fma results, so the max needs no NaN
+  // quieting): the reference is raised -- O and the sums rescaled -- only when a
+  // t exceeds kTau, so every probability is at most 2^kTau and raises are rare
+  // after the first tile. A raise takes the exact tile max over the query's four
+  // lanes and never lowers the reference; the block's first tile (reference 0,
+  // t = c2*s) always takes it and sets the reference to that max.
+  auto probs = [&](f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
-      // NaN (all of this lane's keys masked on a first tile) also raises
-      if (__any(!(fmaf(mx, a.c2, -m_ref[qb]) <= kTau))) raise_ref(qb, xmax32(xmax16(mx)) * a.c2);
       const float nm = -m_ref[qb];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[qb][kb][r] = fmaf(s[qb][kb][r], a.c2, nm);
+        tm = fmaxf(tm, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
+      }
+      if (fresh || __any(tm > kTau)) {
+        float up = xmax32(xmax16(tm));
+        if (!fresh) up = fmaxf(up, 0.f);
+        raise_ref(qb, up);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[qb][kb] -= up;
+      }
 #pragma unroll
       for (int g = 0; g < BC / 32; ++g) {
         float p[8];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[4 * bb + r] = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * g + bb][r], a.c2, nm));
+          for (int r = 0; r < 4; ++r) p[4 * bb + r] = __builtin_amdgcn_exp2f(s[qb][2 * g + bb][r]);
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
         pf[qb][g] = __builtin_bit_cast(bf16x8, w);
       }
     }
+    fresh = false;
   };
 
   // O^T += V^T P^T from V buffer i, plus the row sums by an all-ones A operand. The V fragments of key group g+1 are requested into

@@ -457,8 +457,10 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // S^T = K Q^T from K buffer i into s, in steps of KH key blocks x one 32-wide
   // d-slice (QB*KH independent accumulators per step); each step's K fragments
   // are requested before the previous step's MFMAs, so the LDS latency hides
-  // behind them (the scheduling barriers keep that order). INT8 keys: logit_j
-  // *= k_scale_j.
+  // behind them (the scheduling barriers keep that order). INT8 keys: the key
+  // scales are folded into the softmax's exponent coefficient, kcs = k_scale *
+  // c2 per key, so the exponent is s * kcs - m_ref (one fma per logit, as for
+  // bf16 keys).
   constexpr int KH = NKB > 4 ? 4 : NKB;
   constexpr int NSTEP = NKB / KH * KK;
   auto read_kstep = [&](int i, int st, bf16x8 (&dst)[KH]) {
@@ -473,6 +475,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   };
   auto read_k0 = [&](int i, bf16x8 (&dst)[KH]) { read_kstep(i, 0, dst); };
   // k0: the first step's fragments, already requested by the caller
+  f32x4 kcs[NKB];   // INT8 cache tiles: per-key exponent coefficients k_scale * c2
   auto logits_from = [&](int i, const bf16x8 (&k0)[KH], f32x4 (&s)[QB][NKB], auto scaled_tag) {
     constexpr bool SCALED = decltype(scaled_tag)::value;
 #pragma unroll
@@ -499,8 +502,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const f32x4 ksv = *reinterpret_cast<const f32x4*>(sc + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] *= ksv;
+        kcs[kb] = ksv * a.c2;
       }
     }
   };
@@ -517,9 +519,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + r >= nvalid)
+        if (32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + r >= nvalid) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
+          kcs[kb][r] = a.c2;   // a zero scale would turn -inf into NaN
+        }
   };
 
   // raise the reference max of query block qb by up (log2 units); the first
@@ -543,7 +547,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // after the first tile. A raise takes the exact tile max over the query's four
   // lanes and never lowers the reference; the block's first tile (reference 0,
   // t = c2*s) always takes it and sets the reference to that max.
-  auto probs = [&](f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32]) {
+  auto probs = [&](f32x4 (&s)[QB][NKB], bf16x8 (&pf)[QB][BC / 32], auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_ref[qb];
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[qb][kb][r] = fmaf(s[qb][kb][r], a.c2, nm);
+        for (int r = 0; r < 4; ++r) s[qb][kb][r] = fmaf(s[qb][kb][r], SCALED ? kcs[kb][r] : a.c2, nm);
         tm = fmaxf(tm, fmaxf(fmaxf(s[qb][kb][0], s[qb][kb][1]), fmaxf(s[qb][kb][2], s[qb][kb][3])));
       }
       if (fresh || __any(tm > kTau)) {
@@ -680,7 +685,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         __syncthreads();
         // H2(t)
         if (grp == 1) issue(t + 2);
-        probs(sacc, pf);
+        probs(sacc, pf, scaled_tag);
         if constexpr (VPF) read_v0(vb(t), vf);
         if (grp == 0) complete(t + 1);
         __syncthreads();
@@ -706,7 +711,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         f32x4 s[QB][NKB];
         logits(i, s, scaled_tag);
         bf16x8 pf[QB][BC / 32];
-        probs(s, pf);
+        probs(s, pf, scaled_tag);
         values(i, pf, no_reads);
         if (more) {
           wait_copies();
@@ -735,7 +740,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     logits(0, s, scaled_tag);
     mask_tail(s, nvalid);
     bf16x8 pf[QB][BC / 32];
-    probs(s, pf);
+    probs(s, pf, scaled_tag);
     values(0, pf, no_reads);
     __syncthreads();
   };

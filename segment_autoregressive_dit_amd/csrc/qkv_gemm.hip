@@ -11,15 +11,18 @@
 //    x rows the B operand (both contiguous along the hidden dimension), so a
 //    lane's accumulator holds 4 consecutive channels of one token -- the RoPE
 //    pairs (2j, 2j+1) sit in one lane and a store writes 8 contiguous bytes.
-//  * Block = 4 waves = 256 channels x 128 tokens, two blocks per CU; each wave
-//    owns 128 x 64 (8 x 4 accumulator tiles). The hidden dimension is walked in
-//    steps of 32: the 256 x 32 and 128 x 32 operand tiles are copied global ->
-//    LDS by the load unit (buffer_load ... lds) into a ring of three stages, one
-//    barrier per step, with the 16-byte chunk index XOR-swizzled by (row/4) % 4.
+//  * Block = 8 waves = 256 channels x 256 tokens, one block per CU; each wave
+//    owns 64 channels x 128 tokens (4 x 8 accumulator tiles). The hidden
+//    dimension is walked in steps of 32: both 256 x 32 operand tiles are copied
+//    global -> LDS by the load unit (buffer_load ... lds) into a ring of four
+//    stages, one barrier per step, with the 16-byte chunk index XOR-swizzled by
+//    (row/4) % 4. (Block, wave tile and ring depth are the NOMAS_GEMM_CFG
+//    defaults below.)
 //  * Software pipeline: a step's MFMAs use fragments read during the previous
 //    step, while they read the next step's fragments (from a stage made
 //    resident by the previous barrier) and the load unit refills the step's own
-//    stage three steps ahead, so a copy has two steps to land.
+//    stage four steps ahead; a step waits only for the copies two steps ahead,
+//    so each copy has three steps to land.
 //  * Blocks are laid out so each XCD works through whole channel tiles: the
 //    W tile stays in that XCD's L2 while token tiles stream past it.
 #include <type_traits>

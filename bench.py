@@ -35,6 +35,8 @@ Also reported (outside the timed steps):
   * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline`` (all the
     BLAS threads), and on one thread over a sample cut by the thread count
     -> ``cpu_baseline.one_thread``.
+``--headline-only`` times the single-layer step and nothing else, so a kernel
+trace of that run holds only the headline's launches.
 Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
 
@@ -68,6 +70,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-denoise", action="store_true", help="skip the 54-layer denoise sweep")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time the single-layer step only (no extra measurements): a kernel trace of this run "
+                        "holds the headline attention launches alone")
     p.add_argument("--cpu-rows", type=int, default=7936, help="query rows per head in the CPU sample")
     return p.parse_args()
 
@@ -502,19 +507,21 @@ def main():
         attention_ms_p10=round(r["attn_ms_p10"], 4),
         attention_ms_p90=round(r["attn_ms_p90"], 4),
     )
-    extra.update(attention_cold_bench())
-    extra.update(long_history_bench())
-    if not args.no_denoise:
+    if not args.headline_only:
+        extra.update(attention_cold_bench())
+        extra.update(long_history_bench())
+    if not args.no_denoise and not args.headline_only:
         d = denoise_bench()
         extra.update(denoise_sparse_ms_per_step=round(d["denoise_sparse_ms_per_step"], 3),
                      denoise_sparse_n_select=d["denoise_sparse_n_select"])
         extra.update(denoise_ms_per_step=round(d["denoise_ms_per_step"], 3),
                      denoise_attention_tflops=round(d["denoise_tflops"], 1),
                      denoise_append_ms_per_turn=round(d["denoise_append_ms_per_turn"], 3))
-    extra.update(block_causal_bench())
-    extra.update(sparse_layer_bench())
-    extra.update(archive_bench())
-    extra.update(qkv_bench())
+    if not args.headline_only:
+        extra.update(block_causal_bench())
+        extra.update(sparse_layer_bench())
+        extra.update(archive_bench())
+        extra.update(qkv_bench())
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
     line = {
         "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",

@@ -145,7 +145,7 @@ def bf16_bits_to_f64(u):
     return u.view(np.float32).astype(np.float64)
 
 
-def rising_logit_inputs(n_heads, head_dim, n_cached, n_cur, seed, growth_log2=140.0, block=64):
+def rising_logit_inputs(n_heads, head_dim, n_cached, n_cur, seed, growth_log2=140.0, block=64, mixed=False):
     """Inputs whose attention logits climb steeply along the key order.
 
     Every query is a per-head sign pattern u (entries +-1) plus N(0, 0.05^2)
@@ -155,8 +155,12 @@ def rising_logit_inputs(n_heads, head_dim, n_cached, n_cur, seed, growth_log2=14
     grows by about ``growth_log2`` from one run to the next; the key's place in
     run b is (7b + 3) mod block, so it visits every position class. A running
     softmax maximum that is not raised on some run overflows exp2 at once.
-    Values are N(0, 1). Returns bf16 patterns (q [n_cur,H,D], k_cache, v_cache
-    [n_cached,H,D], k_cur, v_cur [n_cur,H,D])."""
+    Values are N(0, 1). With ``mixed``, odd query rows are negated (their
+    logits fall along the key order) and run 0 holds one more key, -a_0 * u at
+    place 5, so that those rows' largest logit sits in the first run, about
+    ``growth_log2`` above everything after it, while the even rows still climb.
+    Returns bf16 patterns (q [n_cur,H,D], k_cache, v_cache [n_cached,H,D],
+    k_cur, v_cur [n_cur,H,D])."""
     rng = np.random.default_rng(np.random.SeedSequence([9001, seed]))
     H, D = n_heads, head_dim
     u = rng.choice(np.array([-1.0, 1.0], np.float32), size=(H, D))
@@ -168,6 +172,10 @@ def rising_logit_inputs(n_heads, head_dim, n_cached, n_cur, seed, growth_log2=14
         j = b * block + (7 * b + 3) % block
         if j < n_k:
             k[j] = np.float32(growth_log2 * (b + 1) / per_unit) * u
+    if mixed:
+        q[1::2] *= np.float32(-1.0)
+        if 5 < min(block, n_k):
+            k[5] = np.float32(-growth_log2 / per_unit) * u
     v = rng.standard_normal((n_k, H, D), dtype=np.float32)
     kb, vb = _round_bf16_bits(k), _round_bf16_bits(v)
     return _round_bf16_bits(q), kb[:n_cached], vb[:n_cached], kb[n_cached:], vb[n_cached:]

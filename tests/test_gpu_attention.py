@@ -239,6 +239,37 @@ def test_rising_logits_raise_reference(D, int8, splits):
 
 @pytest.mark.parametrize("int8", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
+def test_rising_and_falling_logits_in_one_wave(D, int8):
+    """Even query rows climb as above while odd rows peak in the first tile and
+    fall about 140 (log2 units) below that peak afterwards: every later tile
+    raises the reference for the even rows of a wave but must leave the odd
+    rows' reference where it is (a raise that lowered it would rescale their
+    output by about 2^140 and overflow)."""
+    H, tpf, frames, nv, nt = 2, 64, 12, 128, 16
+    n_cached = frames * tpf
+    q_b, kc_b, vc_b, kn_b, vn_b = synth.rising_logit_inputs(H, D, n_cached, nv + nt, seed=5 + D + 2 * int8,
+                                                            mixed=True)
+    say(f"attention: rising and falling logits D={D} int8={int8}")
+    cache = nomas.KVCache(H, D, tpf, frames, int8)
+    cache.nomas_kvcache_append(dev_bf16(kc_b), dev_bf16(vc_b), frames)
+    lse = torch.empty(H * (nv + nt), dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention(dev_bf16(q_b), dev_bf16(kn_b), dev_bf16(vn_b), nv, nt, cache, lse=lse,
+                                        n_splits=1)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    assert np.all(np.isfinite(got)), "non-finite output: a raise moved some query's reference down"
+    kp, vp = synth.bf16_bits_to_f64(kc_b), synth.bf16_bits_to_f64(vc_b)
+    if int8:
+        kp, vp = quant.dequantise(*quant.quantise(kp)), quant.dequantise(*quant.quantise(vp))
+    x = [synth.bf16_bits_to_f64(t) for t in (q_b, kn_b, vn_b)]
+    ref, ref_lse = attention.segment_attention(x[0], x[1], x[2], kp, vp, 1.0 / math.sqrt(D))
+    _check(got, ref, f"rising and falling logits D={D} int8={int8}")
+    g_lse = lse.cpu().numpy().reshape(H, nv + nt)
+    assert np.max(np.abs(g_lse - ref_lse)) <= LSE_TOL + 1e-3, np.max(np.abs(g_lse - ref_lse))
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
 def test_values_of_one_key_range(D, int8):
     """Values nonzero in one key range at a time (a full cache tile, the partial
     last cache tile, a full current tile, the partial last current tile), with

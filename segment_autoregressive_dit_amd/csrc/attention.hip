@@ -829,31 +829,37 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   if (lse && d0 == 0) lse[(int64_t)h * n_q + row] = m + logf(wsum);
 }
 
-// ---- current segment's V -> V^T [H][D][pitch] (zero beyond n)
+// ---- current segment's V -> V^T [H][D][pitch] (zero beyond n). A lane moves an
+// 8 x 8 block (8 tokens x 8 channels): eight 16-byte row loads, a transpose in
+// registers (each output word joins two 16-bit halves), eight 16-byte stores;
+// no LDS. A block is 128 tokens x D channels of one head, one wave per 64 x 64
+// quarter; lane = 8 * channel chunk + token group, so a load instruction reads
+// 8 rows x 128 contiguous bytes and a store writes 8 channel rows x 128
+// contiguous bytes.
 template <int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v, int64_t ld, int n,
-                                                          uint16_t* __restrict__ vt, int pitch) {
-  constexpr int TT = 64;                      // tokens per block
-  constexpr int RP = TT + 8;                  // padded LDS row (elements)
-  __shared__ __align__(16) uint16_t tile[D * RP];
-  const int h = blockIdx.y, t0 = blockIdx.x * TT;
-  for (int c = threadIdx.x; c < TT * D / 8; c += 256) {
-    const int t = c / (D / 8), cc = c % (D / 8);
-    u32x4 x = {0, 0, 0, 0};
-    if (t0 + t < n) x = *reinterpret_cast<const u32x4*>(v + (int64_t)(t0 + t) * ld + (int64_t)h * D + cc * 8);
+__global__ __launch_bounds__(2 * D) void v_transpose_kernel(const uint16_t* __restrict__ v, int64_t ld, int n,
+                                                           uint16_t* __restrict__ vt, int pitch) {
+  const int h = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * 128 + (wave & 1) * 64 + 8 * (lane & 7);   // the lane's first token
+  const int d0 = (wave >> 1) * 64 + 8 * (lane >> 3);                     // and first channel
+  u32x4 in[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[(cc * 8 + 2 * e) * RP + t] = static_cast<uint16_t>(x[e] & 0xffffu);
-      tile[(cc * 8 + 2 * e + 1) * RP + t] = static_cast<uint16_t>(x[e] >> 16);
-    }
+  for (int i = 0; i < 8; ++i) {   // rows past n (n >= 1) read row n-1 and keep zeros
+    in[i] = *reinterpret_cast<const u32x4*>(v + (int64_t)min(t0 + i, n - 1) * ld + (int64_t)h * D + d0);
+    if (t0 + i >= n) in[i] = (u32x4){0, 0, 0, 0};
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < D * (TT / 8); i += 256) {
-    const int d = i / (TT / 8), g = i % (TT / 8);
-    *reinterpret_cast<u32x4*>(vt + ((int64_t)h * D + d) * pitch + t0 + 8 * g) =
-        *reinterpret_cast<const u32x4*>(&tile[d * RP + 8 * g]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = in[2 * k][j >> 1], b = in[2 * k + 1][j >> 1];
+      o[k] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    *reinterpret_cast<u32x4*>(vt + ((int64_t)h * D + d0 + j) * pitch + t0) = o;
   }
 }
+static_assert(kTokenAlign % 128 == 0, "V^T pitches are whole 128-token blocks");
 
 // ---------------------------------------------------------------- host side
 struct Plan {
@@ -1003,9 +1009,9 @@ static int32_t segment_attention_impl(const uint16_t* q, const uint16_t* k_cur, 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws);
   {
-    const dim3 grid((unsigned)(p.pitch_cur / 64), (unsigned)H);
+    const dim3 grid((unsigned)(p.pitch_cur / 128), (unsigned)H);
     if (D == 128) hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, v_cur, ld_qkv, p.n_q, vt, p.pitch_cur);
-    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, st, v_cur, ld_qkv, p.n_q, vt, p.pitch_cur);
+    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(128), 0, st, v_cur, ld_qkv, p.n_q, vt, p.pitch_cur);
     if (int32_t e = check_launch("segment_attention (v transpose)")) return e;
   }
 
@@ -1170,9 +1176,9 @@ extern "C" int32_t nomas_block_causal_attention(const uint16_t* q, const uint16_
   const hipStream_t st = as_stream(stream);
   uint16_t* vt = static_cast<uint16_t*>(workspace);
   {
-    const dim3 grid((unsigned)(p.pitch / 64), (unsigned)H);
+    const dim3 grid((unsigned)(p.pitch / 128), (unsigned)H);
     if (D == 128) hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, v, ld_qkv, p.n_rows, vt, p.pitch);
-    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, st, v, ld_qkv, p.n_rows, vt, p.pitch);
+    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(128), 0, st, v, ld_qkv, p.n_rows, vt, p.pitch);
     if (int32_t e = check_launch("block_causal_attention (v transpose)")) return e;
   }
   AttnArgs a{};

@@ -14,11 +14,12 @@
 // An append of n frames writes only its last min(n, capacity) frames, so no two
 // tokens of one launch target the same slot and the launch is race-free.
 //
-// Kernel: one block = 64 tokens of one head. Each token's head_dim values are
-// spread over head_dim/8 consecutive lanes (16-byte chunks), which reduce the
-// absmax with lane shuffles. K rows are written token-major; V is written
+// INT8 kernel: one block = 64 tokens of one head. Each token's head_dim values
+// are spread over head_dim/8 consecutive lanes (16-byte chunks), which reduce
+// the absmax with lane shuffles. K rows are written token-major; V is written
 // transposed ([head][dim][token]) through an LDS tile so that each wave stores
-// whole 64-token runs of one dim.
+// whole 64-token runs of one dim. The BF16 cache has a copy kernel of its own
+// (kv_append_bf16_kernel, below).
 #include "nomas_common.hpp"
 
 namespace nomas {
@@ -52,13 +53,12 @@ __device__ __forceinline__ int slot_token(const AppendArgs& a, int r) {
 // Correctly rounded float32 quotient; the build keeps IEEE division (no fast-math).
 __device__ __forceinline__ float div_rn(float x, float y) { return x / y; }
 
-template <int D, bool INT8, bool VEC4>
+template <int D, bool VEC4>
 __global__ __launch_bounds__(kAppThreads) void kv_append_kernel(AppendArgs a) {
   constexpr int CPR = D / 8;                       // chunks per token row
   constexpr int CHUNKS = kAppTok * CPR;
   constexpr int PER_THREAD = CHUNKS / kAppThreads;
-  constexpr int ESZ = INT8 ? 1 : 2;
-  constexpr int ROWB = kAppTok * ESZ + 16;         // padded LDS row of the V^T tile (bytes)
+  constexpr int ROWB = kAppTok + 16;               // padded LDS row of the V^T code tile (bytes)
   __shared__ __align__(16) unsigned char vt[D * ROWB];
   __shared__ int slots[kAppTok];
 
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kAppThreads) void kv_append_kernel(AppendArgs a) {
     }
     const int st = slots[t];
     const int64_t krow = ((int64_t)h * a.pitch + st) * D + cc * 8;
-    if (INT8) {
+    {
       float kf[8], vf[8];
       float km = 0.f, vm = 0.f;
 #pragma unroll
@@ -119,13 +119,6 @@ __global__ __launch_bounds__(kAppThreads) void kv_append_kernel(AppendArgs a) {
           a.vs[(int64_t)h * a.pitch + st] = vsc;
         }
       }
-    } else {
-      if (live) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.kc) + krow) = kx;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(&vt[(cc * 8 + 2 * e) * ROWB + 2 * t]) = static_cast<uint16_t>(vx[e] & 0xffffu);
-        *reinterpret_cast<uint16_t*>(&vt[(cc * 8 + 2 * e + 1) * ROWB + 2 * t]) = static_cast<uint16_t>(vx[e] >> 16);
-      }
     }
   }
   __syncthreads();
@@ -139,31 +132,81 @@ __global__ __launch_bounds__(kAppThreads) void kv_append_kernel(AppendArgs a) {
     if (t >= n_live) continue;
     const int64_t vrow = ((int64_t)h * D + d) * a.pitch;
     if (VEC4) {   // 4 tokens of one frame, contiguous and aligned slots
-      if (INT8)
-        *reinterpret_cast<unsigned*>(static_cast<int8_t*>(a.vc) + vrow + slots[t]) =
-            *reinterpret_cast<const unsigned*>(&vt[d * ROWB + t]);
-      else
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.vc) + vrow + slots[t]) =
-            *reinterpret_cast<const uint2*>(&vt[d * ROWB + 2 * t]);
+      *reinterpret_cast<unsigned*>(static_cast<int8_t*>(a.vc) + vrow + slots[t]) =
+          *reinterpret_cast<const unsigned*>(&vt[d * ROWB + t]);
     } else {
-      for (int e = 0; e < 4 && t + e < n_live; ++e) {
-        if (INT8)
-          static_cast<int8_t*>(a.vc)[vrow + slots[t + e]] = static_cast<int8_t>(vt[d * ROWB + t + e]);
-        else
-          static_cast<uint16_t*>(a.vc)[vrow + slots[t + e]] =
-              *reinterpret_cast<const uint16_t*>(&vt[d * ROWB + 2 * (t + e)]);
-      }
+      for (int e = 0; e < 4 && t + e < n_live; ++e)
+        static_cast<int8_t*>(a.vc)[vrow + slots[t + e]] = static_cast<int8_t>(vt[d * ROWB + t + e]);
     }
   }
 }
 
-template <int D, bool INT8>
-static void launch_append(const AppendArgs& a, bool vec4, hipStream_t s) {
+// BF16 cache: a plain copy, K rows in place and V transposed in registers. A
+// block is 128 rows x D channels of one head, one wave per 64 x 64 quarter; a
+// lane moves 8 rows x 8 channels: eight 16-byte loads from each of K and V,
+// eight 16-byte K row stores and, after an 8 x 8 transpose, eight 16-byte V^T
+// stores (lane = 8 * channel chunk + row group, so every load and store
+// instruction covers 8 rows of 128 contiguous bytes). VEC8 (tokens per frame a
+// multiple of 8): a lane's 8 rows share a frame and land in 8 consecutive,
+// 16-byte aligned slots; otherwise each row finds its own slot.
+template <int D, bool VEC8>
+__global__ __launch_bounds__(2 * D) void kv_append_bf16_kernel(AppendArgs a) {
+  const int h = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = blockIdx.x * 128 + (wave & 1) * 64 + 8 * (lane & 7);   // the lane's first row
+  const int d0 = (wave >> 1) * 64 + 8 * (lane >> 3);                     // and first channel
+  if (r0 >= a.rows) return;
+  u32x4 kx[8], vx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {   // rows past the end re-read the last row and are not stored
+    const int64_t src = (int64_t)min(r0 + i, a.rows - 1) * a.ld + (int64_t)h * D + d0;
+    kx[i] = *reinterpret_cast<const u32x4*>(a.k_new + src);
+    vx[i] = *reinterpret_cast<const u32x4*>(a.v_new + src);
+  }
+  uint16_t* kc = static_cast<uint16_t*>(a.kc);
+  uint16_t* vc = static_cast<uint16_t*>(a.vc);
+  if constexpr (VEC8) {   // rows is a multiple of tpf, so all 8 rows are live
+    const int s0 = slot_token(a, r0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(kc + ((int64_t)h * a.pitch + s0 + i) * D + d0) = kx[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t x = vx[2 * k][j >> 1], y = vx[2 * k + 1][j >> 1];
+        o[k] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+      }
+      *reinterpret_cast<u32x4*>(vc + ((int64_t)h * D + d0 + j) * a.pitch + s0) = o;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (r0 + i >= a.rows) break;
+      const int st = slot_token(a, r0 + i);
+      *reinterpret_cast<u32x4*>(kc + ((int64_t)h * a.pitch + st) * D + d0) = kx[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        vc[((int64_t)h * D + d0 + j) * a.pitch + st] = static_cast<uint16_t>((j & 1) ? vx[i][j >> 1] >> 16 : vx[i][j >> 1] & 0xffffu);
+    }
+  }
+}
+
+template <int D>
+static void launch_append_bf16(const AppendArgs& a, bool vec8, hipStream_t s) {
+  const dim3 grid((unsigned)((a.rows + 127) / 128), (unsigned)a.n_heads);
+  if (vec8)
+    hipLaunchKernelGGL((kv_append_bf16_kernel<D, true>), grid, dim3(2 * D), 0, s, a);
+  else
+    hipLaunchKernelGGL((kv_append_bf16_kernel<D, false>), grid, dim3(2 * D), 0, s, a);
+}
+
+template <int D>
+static void launch_append_int8(const AppendArgs& a, bool vec4, hipStream_t s) {
   const dim3 grid((unsigned)((a.rows + kAppTok - 1) / kAppTok), (unsigned)a.n_heads);
   if (vec4)
-    hipLaunchKernelGGL((kv_append_kernel<D, INT8, true>), grid, dim3(kAppThreads), 0, s, a);
+    hipLaunchKernelGGL((kv_append_kernel<D, true>), grid, dim3(kAppThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((kv_append_kernel<D, INT8, false>), grid, dim3(kAppThreads), 0, s, a);
+    hipLaunchKernelGGL((kv_append_kernel<D, false>), grid, dim3(kAppThreads), 0, s, a);
 }
 
 int32_t validate_cache(const nomas_kvcache* c, const char* who) {
@@ -218,11 +261,11 @@ extern "C" int32_t nomas_kvcache_append(nomas_kvcache* c, const uint16_t* k_new,
   const hipStream_t s = as_stream(stream);
   const bool int8 = c->kv_dtype == NOMAS_KV_INT8;
   if (D == 128) {
-    if (int8) launch_append<128, true>(a, vec4, s);
-    else launch_append<128, false>(a, vec4, s);
+    if (int8) launch_append_int8<128>(a, vec4, s);
+    else launch_append_bf16<128>(a, tpf % 8 == 0, s);
   } else {
-    if (int8) launch_append<64, true>(a, vec4, s);
-    else launch_append<64, false>(a, vec4, s);
+    if (int8) launch_append_int8<64>(a, vec4, s);
+    else launch_append_bf16<64>(a, tpf % 8 == 0, s);
   }
   if (int32_t e = check_launch("kvcache_append")) return e;
   c->frames_written += n_frames;

@@ -188,11 +188,12 @@ struct AttnCfg {
   static constexpr int VC = BC / 8;                // 16-byte chunks per V^T row (bf16)
   static constexpr int KT_BYTES = BC * D * 2;
   static constexpr int VT_BYTES = D * BC * 2;
-  static constexpr int KSTAGE = KT_BYTES + BC * 4; // K tile + the tile's per-key K scales
+  static constexpr int KSTAGE = KT_BYTES + (I8 ? BC * 4 : 0); // K tile (+ INT8: its per-key K scales)
   static constexpr int VSTAGE = VT_BYTES;          // V^T tile
   static constexpr int NVS = PIPE && VPF ? 3 : 2;  // V^T stages
+  static constexpr int NKS = PIPE && !VPF ? 3 : 2; // K stages
   // INT8: each wave's own copy of a tile's value scales
-  static constexpr int VSC_OFF = 2 * KSTAGE + NVS * VSTAGE;
+  static constexpr int VSC_OFF = NKS * KSTAGE + NVS * VSTAGE;
   static constexpr int VSC_BYTES = I8 ? NW * BC * 4 : 0;
   static constexpr int LDS_BYTES = VSC_OFF + VSC_BYTES;
   static constexpr int NK8 = BC * D / 16 / NT;     // int8 K chunks (16 codes) per thread
@@ -218,10 +219,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   static_assert(kSpKeyBlock % BC == 0 && kSpQueryBlock % C::BR == 0, "sparse blocks must be whole tiles");
   constexpr int NKB = C::NKB, KK = C::KK;
   constexpr int ES = I8 ? 1 : 2;   // bytes per cached element
-  // two K buffers, then C::NVS V^T buffers
+  // C::NKS K buffers, then C::NVS V^T buffers
+  static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) unsigned char lds[C::LDS_BYTES];
   auto kbuf = [&](int i) { return lds + i * C::KSTAGE; };
-  auto vbuf = [&](int i) { return lds + 2 * C::KSTAGE + i * C::VSTAGE; };
+  auto vbuf = [&](int i) { return lds + C::NKS * C::KSTAGE + i * C::VSTAGE; };
 
   const int b = blockIdx.x;
   const int logical = (b & 7) * a.per_xcd + (b >> 3);
@@ -393,6 +395,40 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + blk * 1024), 16,
                                                  d * vstride + c * 16, key0 * 2, 0, 0);
       }
+    }
+  };
+
+  // bf16 tiles copied by the four waves of one group (1 KB blocks gw*KG .. +KG)
+  auto copy_k4 = [&](int t, int i, auto ct) {
+    constexpr bool cache = decltype(ct)::value;
+    constexpr int KG = C::KT_BYTES / 1024 / 4;
+    int key0, nvalid;
+    tile_info(t, ct, key0, nvalid);
+    const __amdgpu_buffer_rsrc_t rk = cache ? rk_c : rk_n;
+    const int kstride = cache ? D * 2 : (int)a.ld_qkv * 2;
+    unsigned char* Ks = kbuf(i);
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int blk = (wave & 3) * KG + k, p = blk * 64 + lane;
+      const int row = p / C::KC, c = (p % C::KC) ^ swz_k<D>(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + blk * 1024), 16,
+                                               row * kstride + c * 16, key0 * kstride, 0, 0);
+    }
+  };
+  auto copy_v4 = [&](int t, int i, auto ct) {
+    constexpr bool cache = decltype(ct)::value;
+    constexpr int VG = C::VT_BYTES / 1024 / 4;
+    int key0, nvalid;
+    tile_info(t, ct, key0, nvalid);
+    const __amdgpu_buffer_rsrc_t rv = cache ? rv_c : rv_n;
+    const int vstride = (cache ? a.pitch_c : a.pitch_cur) * 2;
+    unsigned char* Vs = vbuf(i);
+#pragma unroll
+    for (int k = 0; k < VG; ++k) {
+      const int blk = (wave & 3) * VG + k, p = blk * 64 + lane;
+      const int d = p / C::VC, c = (p % C::VC) ^ swz_v<BC>(d);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + blk * 1024), 16,
+                                               d * vstride + c * 16, key0 * 2, 0, 0);
     }
   };
 
@@ -621,14 +657,59 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   auto no_reads = []() {};
 
   // ---- a run of n full tiles [t0, t0+n) of one kind.
-  // PIPE: step j does the softmax and value MFMAs of tile j beside the logit
-  // MFMAs and row max of tile j+1, while K(j+2) and V(j+1) are in flight.
-  // Otherwise: tile by tile, the next tile's copies in flight during its MFMAs.
+  // PIPE: two wave groups in ping-pong, one issuing MFMAs while the other runs
+  // the softmax. bf16 tiles of the cached and sparse calls take the three-K-stage
+  // schedule (no copies in the MFMA phases); INT8 cache tiles and the
+  // multi-segment call (whose kernel has no registers to spare for it) take the
+  // two-stage one. Otherwise: tile by tile, the next tile's copies in flight
+  // during its MFMAs.
   auto run_full = [&](int t0, int n, auto ct) {
     if (n <= 0) return;
     const std::bool_constant<I8 && decltype(ct)::value> scaled_tag;
-    if constexpr (PIPE) {
-      // Ping-pong: each tile is an MFMA phase H1(t) = [values of t-1, logits of
+    if constexpr (PIPE && !VPF && !I8 && !MS) {
+      // bf16 ping-pong, three K stages. Slot X(t) = [A: H1(t) | B: H2(t-1)],
+      // slot Y(t) = [A: H2(t) | B: H1(t)]; H1 = values of t-1 + logits of t (MFMA),
+      // H2 = softmax of t. The MFMA phases issue no copies: A copies K(t+2)
+      // whole at the top of its H2(t) (slot Y(t); K buffer (t+2)%3 was last read
+      // in slot Y(t-1)) and waits for K(t+1) at its end; B copies V(t+1) whole at
+      // the top of its H2(t) (slot X(t+1); V buffer (t+1)%2 was last read in slot
+      // Y(t)) and waits for it at the end of its H1(t+1).
+      constexpr int KG = C::KT_BYTES / 1024 / 4;
+      const int grp = PP_GROUP(wave);
+      start_k(t0, 0, ct);
+      if (n > 1) start_k(t0 + 1, 1, ct);
+      start_v(t0, 0, ct);
+      wait_copies();
+      __syncthreads();
+      f32x4 sacc[QB][NKB];
+      bf16x8 pf[QB][BC / 32];
+      if (grp == 1) __syncthreads();   // group B runs one slot behind
+      int kb = 0;                      // K buffer of tile t: t % 3
+      for (int t = 0; t < n; ++t) {
+        __builtin_amdgcn_s_setprio(1);
+        bf16x8 k0[KH];
+        if (t >= 1) values((t - 1) & 1, pf, [&]() { read_k0(kb, k0); });
+        else read_k0(kb, k0);
+        logits_from(kb, k0, sacc, scaled_tag);
+        __builtin_amdgcn_s_setprio(0);
+        if (grp == 1) wait_copies();
+        __syncthreads();
+        const int kb2 = kb == 0 ? 2 : kb - 1;   // (t + 2) % 3
+        if (grp == 0 && t + 2 < n) copy_k4(t0 + t + 2, kb2, ct);
+        if (grp == 1 && t + 1 < n) copy_v4(t0 + t + 1, (t + 1) & 1, ct);
+        probs(sacc, pf, scaled_tag);
+        if (grp == 0) {
+          if (t + 2 < n) __builtin_amdgcn_s_waitcnt((KG & 15) | (7 << 4) | ((KG >> 4) << 14));
+          else wait_copies();
+        }
+        __syncthreads();
+        kb = kb == 2 ? 0 : kb + 1;
+      }
+      values((n - 1) & 1, pf, no_reads);
+      __syncthreads();
+      if (grp == 0) __syncthreads();   // group A's idle last slot
+    } else if constexpr (PIPE) {
+      // Two-stage ping-pong: each tile is an MFMA phase H1(t) = [values of t-1, logits of
       // t] and a VALU phase H2(t) = [softmax of t]. The two wave groups (one wave
       // of each on every SIMD) run one barrier apart, so in every slot one group
       // issues MFMAs while the other runs the softmax. K(s) is issued in slot

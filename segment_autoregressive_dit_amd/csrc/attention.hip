@@ -20,22 +20,27 @@
 //    O^T += V^T P^T, so P never goes through LDS.
 //  * V^T operand rows are contiguous key runs: the cache stores V transposed and
 //    the current segment's V is transposed once into the workspace.
-//  * K and V^T tiles of BC keys are double-buffered in LDS (INT8: three V^T
-//    stages), with the 16-byte chunk index XOR-swizzled by the row so that the
-//    strided 128-bit operand reads are bank-conflict free. bf16 tiles are copied
-//    global -> LDS by the load unit (buffer_load ... lds).
+//  * K and V^T tiles of BC keys are staged in LDS, with the 16-byte chunk index
+//    XOR-swizzled by the row so that the strided 128-bit operand reads are
+//    bank-conflict free: three K and two V^T stages (all 160 KB) for bf16 tiles
+//    of the cached and sparse calls, two K stages otherwise (INT8: three V^T
+//    stages). bf16 tiles are copied global -> LDS by the load unit
+//    (buffer_load ... lds).
 //  * Head dim 128 runs a ping-pong schedule: the block's 8 waves form two
 //    groups, one wave of each on every SIMD, one barrier apart, so that on every
 //    SIMD one wave issues MFMAs (values of tile t-1, logits of tile t, at issue
-//    priority 1) while the other runs the softmax of its tile. Head dim 64 runs
-//    two 4-wave blocks per CU, tile by tile.
+//    priority 1) while the other runs the softmax of its tile. With three K
+//    stages the copies are all issued from the softmax phases (group A: K two
+//    tiles ahead, group B: V^T one tile ahead). Head dim 64 runs two 4-wave
+//    blocks per CU, tile by tile.
 //  * Online softmax in the log2 domain with a fixed reference max per query that
 //    is only raised when a tile's max exceeds it by more than kTau (probabilities
 //    stay <= 2^kTau, exact in fp32 and bf16 range), so the O rescale is rare.
 //  * INT8 cache tiles stage their codes through registers: key codes are
 //    converted to bf16 exactly and the key scale multiplies the fp32 logit of
-//    its key; values are dequantised (code * scale, rounded once to bf16) on the
-//    way into LDS. The scales themselves go global -> LDS by the load unit.
+//    its key (folded into the softmax's exponent coefficient); values are
+//    dequantised (code * scale, rounded once to bf16) on the way into LDS. The
+//    scales themselves go global -> LDS by the load unit.
 //  * Split-KV: the key tiles are cut into contiguous chunks; each block writes a
 //    normalised fp32 partial and its log-sum-exp, merged in fixed order.
 //  * Block ids are remapped so the blocks that the hardware places on one XCD

@@ -41,7 +41,6 @@ Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -474,8 +473,8 @@ def traffic_per_launch():
     try:
         with open(PMC_SUMMARY) as f:
             s = json.load(f)
-        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if s.get("source_sha256") != src:
+        from segment_autoregressive_dit_amd.profile_workload import source_digest
+        if s.get("source_digest") != source_digest(ATTN_SRC):
             return None
         return s["hbm_bytes_per_launch"]
     except Exception:

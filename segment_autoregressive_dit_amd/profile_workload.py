@@ -31,10 +31,21 @@ import collections
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_digest(path):
+    """sha256 of a source file's code with its comments and blank space taken out,
+    so that a counter summary stays matched to a kernel whose comments alone
+    changed (a change to the code itself changes the digest)."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def _dev(bits):
@@ -164,7 +175,7 @@ def cmd_traffic(a):
         "hbm_read_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
         "hbm_bytes_per_launch": fetch_b + write_b,
         "source": a.source,
-        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "source_digest": source_digest(src),
         "command": a.command,
     }
     dur = _dispatch_duration_ns(a.fetch, "FETCH_SIZE", a.kernel)
@@ -195,7 +206,7 @@ def cmd_mfma(a):
         "duration_us_in_counter_run": dur / 1e3 if dur else None,
         "algorithmic_tflops_in_counter_run": a.algorithmic_flop / dur / 1e3 if dur and a.algorithmic_flop else None,
         "source": a.source,
-        "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "source_digest": source_digest(src),
         "command": a.command,
     }
     with open(a.out, "w") as f:

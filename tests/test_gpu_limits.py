@@ -96,3 +96,39 @@ def test_head_slice_just_under_2gib(int8):
     diff = np.abs(got - ref)
     assert diff.max() <= 1e-2 * np.abs(ref).max() and diff.mean() <= 1e-3, (diff.max(), diff.mean())
     assert np.max(np.abs(g_lse - ref_lse)) <= 2.0 ** -8, np.abs(g_lse - ref_lse)
+
+
+def test_current_rows_just_under_2gib():
+    """The current segment's rows read through a row stride that puts their last
+    row's bytes just under 2 GiB from the first (16 rows x 67,108,856 elements x
+    2 B = 2^31 - 256 B): the strided loads of q, k_cur and v_cur reach the end
+    of their 32-bit range. Small cache (the tiny workload); oracle reference."""
+    from oracle import attention
+    from segment_autoregressive_dit_amd import synth
+    from _gpu_util import dev_bf16
+
+    wl = synth.WORKLOADS["tiny"]
+    Hh, Dd, nt = wl.n_heads, wl.head_dim, 16
+    ld = (2 ** 31 - 1) // (nt * 2) // 8 * 8
+    assert nt * ld * 2 < 2 ** 31 and nt * (ld + 8) * 2 >= 2 ** 31
+    say(f"limits: {nt} current rows at row stride {ld} ({nt * ld * 2} B)")
+    cache = nomas.KVCache(Hh, Dd, wl.tpf, wl.capacity_frames, False)
+    kp, vp = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kp), dev_bf16(vp), wl.cached_frames)
+    bits = [synth.normal_bf16((nt, Hh, Dd), 77, 0, 0, tid) for tid in range(3)]
+    views = []
+    for b in bits:
+        full = torch.empty((nt, ld), dtype=torch.bfloat16, device="cuda")
+        full[:, :Hh * Dd] = dev_bf16(b).reshape(nt, Hh * Dd)
+        views.append(full[:, :Hh * Dd])
+    lse = torch.empty(Hh * nt, dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention(views[0], views[1], views[2], 0, nt, cache, lse=lse)
+    torch.cuda.synchronize()
+    got = host_f64(out).reshape(nt, Hh, Dd)
+    x = [synth.bf16_bits_to_f64(b) for b in bits]
+    ref, ref_lse = attention.segment_attention(x[0], x[1], x[2], synth.bf16_bits_to_f64(kp),
+                                               synth.bf16_bits_to_f64(vp), 1.0 / math.sqrt(Dd))
+    diff = np.abs(got - ref)
+    assert diff.max() <= 1e-2 * np.abs(ref).max() and diff.mean() <= 1e-3, (diff.max(), diff.mean())
+    g_lse = lse.cpu().numpy().reshape(Hh, nt)
+    assert np.max(np.abs(g_lse - ref_lse)) <= 2.0 ** -8

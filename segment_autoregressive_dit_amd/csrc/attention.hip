@@ -22,9 +22,8 @@
 //    the current segment's V is transposed once into the workspace.
 //  * K and V^T tiles of BC keys are staged in LDS, with the 16-byte chunk index
 //    XOR-swizzled by the row so that the strided 128-bit operand reads are
-//    bank-conflict free: three K and two V^T stages (all 160 KB) for bf16 tiles
-//    of the cached and sparse calls, two K stages otherwise (INT8: three V^T
-//    stages). bf16 tiles are copied global -> LDS by the load unit
+//    bank-conflict free: three K and two V^T stages (all 160 KB) for bf16
+//    tiles, two K and three V^T stages for INT8. bf16 tiles are copied global -> LDS by the load unit
 //    (buffer_load ... lds).
 //  * Head dim 128 runs a ping-pong schedule: the block's 8 waves form two
 //    groups, one wave of each on every SIMD, one barrier apart, so that on every
@@ -663,15 +662,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
 
   // ---- a run of n full tiles [t0, t0+n) of one kind.
   // PIPE: two wave groups in ping-pong, one issuing MFMAs while the other runs
-  // the softmax. bf16 tiles of the cached and sparse calls take the three-K-stage
-  // schedule (no copies in the MFMA phases); INT8 cache tiles and the
-  // multi-segment call (whose kernel has no registers to spare for it) take the
-  // two-stage one. Otherwise: tile by tile, the next tile's copies in flight
-  // during its MFMAs.
+  // the softmax. bf16 tiles take the three-K-stage schedule (no copies in the
+  // MFMA phases), INT8 cache tiles the two-stage one. Otherwise: tile by tile,
+  // the next tile's copies in flight during its MFMAs.
   auto run_full = [&](int t0, int n, auto ct) {
     if (n <= 0) return;
     const std::bool_constant<I8 && decltype(ct)::value> scaled_tag;
-    if constexpr (PIPE && !VPF && !I8 && !MS) {
+    if constexpr (PIPE && !VPF && !I8) {
       // bf16 ping-pong, three K stages. Slot X(t) = [A: H1(t) | B: H2(t-1)],
       // slot Y(t) = [A: H2(t) | B: H1(t)]; H1 = values of t-1 + logits of t (MFMA),
       // H2 = softmax of t. The MFMA phases issue no copies: A copies K(t+2)

@@ -711,57 +711,50 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       __syncthreads();
       if (grp == 0) __syncthreads();   // group A's idle last slot
     } else if constexpr (PIPE) {
-      // Two-stage ping-pong: each tile is an MFMA phase H1(t) = [values of t-1, logits of
-      // t] and a VALU phase H2(t) = [softmax of t]. The two wave groups (one wave
-      // of each on every SIMD) run one barrier apart, so in every slot one group
-      // issues MFMAs while the other runs the softmax. K(s) is issued in slot
-      // 2s-2 and completes at the end of slot 2s-1, into K buffer s%2. V(s)
-      // follows one tile later into V buffer s%2 -- or, with VPF, travels with
-      // K(s) into V buffer s%3, so that each wave's H2(s) can already request
-      // V(s)'s first fragments for its next H1, across the barrier.
+      // INT8 ping-pong, two K stages and three V^T stages: each tile is an MFMA
+      // phase H1(t) = [values of t-1, logits of t] and a VALU phase H2(t) =
+      // [softmax of t], the two groups one barrier apart. K(s) and V(s) travel
+      // together: group A loads its half at the top of its H1(s-1), group B at
+      // the top of its H2(s-2), and each converts its half into K buffer s%2 and
+      // V buffer s%3 before the barrier that opens A's H1(s). With the third V
+      // stage each wave's H2(s) already requests V(s)'s first fragments for its
+      // next H1, across the barrier.
+      static_assert(VPF, "the two-stage schedule serves INT8 tiles, whose K and V travel together");
       const int grp = PP_GROUP(wave);
-      auto vb = [](int s) { return VPF ? s % 3 : s & 1; };
       auto issue = [&](int s) {
-        if (s < n) start_k(t0 + s, s & 1, ct);
-        const int sv = VPF ? s : s - 1;
-        if (sv >= 0 && sv < n) start_v(t0 + sv, vb(sv), ct);
+        if (s < n) {
+          start_k(t0 + s, s & 1, ct);
+          start_v(t0 + s, s % 3, ct);
+        }
       };
       auto complete = [&](int s) {
         wait_copies();
-        if (s < n) finish_k(t0 + s, s & 1, ct);
-        const int sv = VPF ? s : s - 1;
-        if (sv >= 0 && sv < n) finish_v(t0 + sv, vb(sv), ct);
+        if (s < n) {
+          finish_k(t0 + s, s & 1, ct);
+          finish_v(t0 + s, s % 3, ct);
+        }
       };
       start_k(t0, 0, ct);
-      if constexpr (VPF) start_v(t0, 0, ct);
+      start_v(t0, 0, ct);
       wait_copies();
       finish_k(t0, 0, ct);
-      if constexpr (VPF) finish_v(t0, 0, ct);
+      finish_v(t0, 0, ct);
       __syncthreads();
       f32x4 sacc[QB][NKB];
       bf16x8 pf[QB][BC / 32];
-      bf16x8 vf[VPF ? D / 16 : 1];
+      bf16x8 vf[D / 16];
       if (grp == 1) {     // group B's idle first slot
         issue(1);
         __syncthreads();
       }
       for (int t = 0; t < n; ++t) {
-        // H1(t). The MFMA wave takes issue priority over the softmax wave on its
-        // SIMD, so each MFMA goes out as soon as the matrix core frees. Group A's
-        // copies for the next tile are split around the value MFMAs (keys first,
-        // values after), so neither batch of copy issues delays many MFMAs.
+        // H1(t), at issue priority 1 so that each MFMA goes out as soon as the
+        // matrix core frees
         __builtin_amdgcn_s_setprio(1);
-        if (grp == 0 && t + 1 < n) start_k(t0 + t + 1, (t + 1) & 1, ct);
-        if (VPF && grp == 0 && t + 1 < n) start_v(t0 + t + 1, vb(t + 1), ct);
+        if (grp == 0) issue(t + 1);
         bf16x8 k0[KH];   // first K fragments of tile t, landing during the value MFMAs
-        if constexpr (VPF) {
-          read_k0(t & 1, k0);
-          if (t >= 1) values_from(vb(t - 1), pf, vf);
-        } else {
-          if (t >= 1) values(vb(t - 1), pf, [&]() { read_k0(t & 1, k0); });
-          else read_k0(t & 1, k0);
-          if (grp == 0 && t < n) start_v(t0 + t, vb(t), ct);
-        }
+        read_k0(t & 1, k0);
+        if (t >= 1) values_from((t - 1) % 3, pf, vf);
         logits_from(t & 1, k0, sacc, scaled_tag);
         __builtin_amdgcn_s_setprio(0);
         if (grp == 1) complete(t + 1);
@@ -769,12 +762,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         // H2(t)
         if (grp == 1) issue(t + 2);
         probs(sacc, pf, scaled_tag);
-        if constexpr (VPF) read_v0(vb(t), vf);
+        read_v0(t % 3, vf);
         if (grp == 0) complete(t + 1);
         __syncthreads();
       }
-      if constexpr (VPF) values_from(vb(n - 1), pf, vf);
-      else values(vb(n - 1), pf, no_reads);
+      values_from((n - 1) % 3, pf, vf);
       __syncthreads();
       if (grp == 0) __syncthreads();   // group A's idle last slot
     } else {

@@ -456,17 +456,18 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       }
     }
   };
-  auto finish_v = [&](int t, int i, auto ct) {
+  // INT8: the value scales of the lane's 16 keys (keys 16*cc .. 16*cc+15)
+  auto read_vsc = [&](f32x4 (&sc)[4]) {
+    const int cc = lane % (BC / 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[e] = *reinterpret_cast<const f32x4*>(vsc() + (cc * 16 + 4 * e) * 4);
+  };
+  auto finish_v_sc = [&](int t, int i, auto ct, const f32x4 (&sc)[4]) {
     constexpr bool cache = decltype(ct)::value;
-    int key0, nvalid;
-    tile_info(t, ct, key0, nvalid);
     if constexpr (I8 && cache) {
       unsigned char* Vs = vbuf(i);
       // a lane's chunks all cover keys 16*cc .. 16*cc+15
       const int cc = lane % (BC / 16);
-      f32x4 sc[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = *reinterpret_cast<const f32x4*>(vsc() + (cc * 16 + 4 * e) * 4);
 #pragma unroll
       for (int j = 0; j < C::NV8; ++j) {
         const int d = ((j * NW + wave) * 64 + lane) / (BC / 16);
@@ -478,6 +479,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  auto finish_v = [&](int t, int i, auto ct) {
+    f32x4 sc[4];
+    if constexpr (I8 && decltype(ct)::value) read_vsc(sc);
+    finish_v_sc(t, i, ct, sc);
   };
   auto wait_copies = [&]() { __builtin_amdgcn_s_waitcnt(0); };
 
@@ -727,11 +733,15 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
           start_v(t0 + s, s % 3, ct);
         }
       };
+      // (the value scales are requested first: their LDS latency hides behind
+      // the key conversion)
       auto complete = [&](int s) {
         wait_copies();
         if (s < n) {
+          f32x4 sc[4];
+          if constexpr (decltype(ct)::value) read_vsc(sc);
           finish_k(t0 + s, s & 1, ct);
-          finish_v(t0 + s, s % 3, ct);
+          finish_v_sc(t0 + s, s % 3, ct, sc);
         }
       };
       start_k(t0, 0, ct);

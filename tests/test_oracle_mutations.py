@@ -5,9 +5,13 @@ tests/test_oracle_*.py must then fail. This shows the pins bind the oracle's
 arithmetic instead of restating it."""
 
 import math
+import sys
 
 import numpy as np
 import pytest
+
+if sys.version_info < (3, 11):
+    from exceptiongroup import BaseExceptionGroup
 
 import test_oracle_attention as PA
 import test_oracle_formats as PF
@@ -21,12 +25,17 @@ from oracle import attention, formats, qkv, quant, ring, rope, sparse
 
 def _some_pin_fails(pins):
     # only a failed assertion counts: a planted slip that merely crashes would
-    # say nothing about the pins
+    # say nothing about the pins (a property-based pin that finds several
+    # distinct failing examples reports them together, as a group)
     for pin in pins:
         try:
             pin()
         except AssertionError:
             return True
+        except BaseExceptionGroup as eg:
+            if all(isinstance(e, AssertionError) for e in eg.exceptions):
+                return True
+            raise
     return False
 
 
@@ -116,7 +125,10 @@ def _attention_variant(slip):
             k_past = v_past = None
         if slip == "keys_as_values":
             v_cur, v_past = k_cur, k_past
-        return orig(q, k_cur, v_cur, k_past, v_past, scale, return_probs)
+        res = orig(q, k_cur, v_cur, k_past, v_past, scale, return_probs)
+        if slip == "lse_log2":
+            return (res[0], res[1] / math.log(2.0)) + tuple(res[2:])
+        return res
     return seg
 
 
@@ -206,6 +218,20 @@ class _RingKeepsOldest(ring.RingModel):
                 self.evicted.append(self.frames.pop())               # evicts the newest
 
 
+class _RingOneShort(ring.RingModel):
+    def append(self, payloads):
+        for p in payloads:
+            self.frames.append((self.frames_written, p))
+            self.frames_written += 1
+            while len(self.frames) >= self.capacity:              # keeps capacity-1 frames
+                self.evicted.append(self.frames.pop(0))
+
+
+class _RingSlotsFromOne(ring.RingModel):
+    def expected_slots(self):
+        return {(f + 1) % self.capacity: (f, p) for f, p in self.frames}
+
+
 # ---- format slip
 def _to_bf16_truncate(x):
     f = np.asarray(x, dtype=np.float64).astype(np.float32)
@@ -224,6 +250,7 @@ MUTANTS = {
     "attention: scale dropped": (attention, "segment_attention", _attention_variant("no_scale"), ATTN_PINS),
     "attention: cached keys dropped": (attention, "segment_attention", _attention_variant("drop_past"), ATTN_PINS),
     "attention: keys used as values": (attention, "segment_attention", _attention_variant("keys_as_values"), ATTN_PINS),
+    "attention: log-sum-exp in log2 units": (attention, "segment_attention", _attention_variant("lse_log2"), ATTN_PINS),
     "attention: softmax not normalised": (attention, "_softmax_rows", _softmax_no_normalisation, ATTN_PINS),
     "attention: split weights not normalised": (attention, "split_attention", _split_unnormalised_weights, ATTN_PINS),
     "attention: window mask off by one": (attention, "block_causal_full", _block_causal_window_off_by_one(), ATTN_PINS),
@@ -235,6 +262,8 @@ MUTANTS = {
     "qkv: RoPE applied to values": (qkv, "qkv_projection", _qkv_variant("rope_on_values"), QKV_PINS),
     "qkv: q and k blocks exchanged": (qkv, "qkv_projection", _qkv_variant("qk_swapped"), QKV_PINS),
     "ring: evicts the newest frame": (ring, "RingModel", _RingKeepsOldest, RING_PINS),
+    "ring: window one frame short": (ring, "RingModel", _RingOneShort, RING_PINS),
+    "ring: slots counted from one": (ring, "RingModel", _RingSlotsFromOne, RING_PINS),
     "formats: bf16 by truncation": (formats, "to_bf16", _to_bf16_truncate, FORMAT_PINS),
 }
 

@@ -68,7 +68,8 @@ def _crafted_frame(tpf, H, D, seed):
     from_bits = synth.bf16_bits_to_f64
     for h in range(H):
         x[0, h] = 0.0
-        for t, mb in ((1, 0x3F96), (2, 0x3FB4), (3, 0x0081), (4, 0x7E80), (5, 0x3F80)):
+        # (0x3A8F: the float32 scale lies above m/127, so m/2 codes to 63, not 64)
+        for t, mb in ((1, 0x3F96), (2, 0x3FB4), (3, 0x0081), (4, 0x7E80), (5, 0x3F80), (9, 0x3A8F)):
             m = np.float32(from_bits(np.array([mb], np.uint16))[0])
             x[t, h] = x[t, h] * (m / 8)
             x[t, h, 0] = m

@@ -45,7 +45,7 @@ ROPE_PINS = [PR.test_positions_match_explicit_loops, PR.test_pair_norms_preserve
 QUANT_PINS = [PQ.test_roundtrip_within_half_step, PQ.test_special_cases, PQ.test_ties_round_to_even,
               PQ.test_every_code_is_exact_in_bf16] + \
              [lambda m=m: PQ.test_exhaustive_against_exact_rational(m)
-              for m in (0x3F80, 0x4080, 0x40A0, 0x42A0, 0x3A83, 0x0081, 0x3F96, 0x3FB4)]
+              for m in (0x3F80, 0x4080, 0x40A0, 0x42A0, 0x3A83, 0x0081, 0x3F96, 0x3FB4, 0x3A8F)]
 ATTN_PINS = [PA.test_probability_rows_sum_to_one, PA.test_ones_values_give_ones,
              PA.test_constant_keys_give_mean_and_frame_histogram, PA.test_single_key_and_dominant_logit,
              PA.test_key_permutation_invariance, PA.test_brute_force_tiny] + \
@@ -98,12 +98,12 @@ def _positions_hw_swapped(t0, n_frames, grid_h, grid_w):
 
 
 # ---- quantisation slips
-def _quantise_variant(div=127.0, rounding="even", f32_quotient=True):
+def _quantise_variant(div=127.0, rounding="even", f32_quotient=True, f32_scale=True):
     def q(x):
         x = np.asarray(x, dtype=np.float64)
         m = np.max(np.abs(x), axis=-1)
         s = (m / div).astype(np.float32)
-        s64 = s.astype(np.float64)
+        s64 = s.astype(np.float64) if f32_scale else m / div
         safe = np.where(s64 > 0, s64, 1.0)[..., None]
         r = x / safe
         if f32_quotient:
@@ -247,6 +247,7 @@ MUTANTS = {
     "quant: scale absmax/128": (quant, "quantise", _quantise_variant(div=128.0), QUANT_PINS),
     "quant: ties away from zero": (quant, "quantise", _quantise_variant(rounding="away"), QUANT_PINS),
     "quant: quotient not rounded to fp32": (quant, "quantise", _quantise_variant(f32_quotient=False), QUANT_PINS),
+    "quant: codes against the unrounded scale": (quant, "quantise", _quantise_variant(f32_scale=False), QUANT_PINS),
     "attention: scale dropped": (attention, "segment_attention", _attention_variant("no_scale"), ATTN_PINS),
     "attention: cached keys dropped": (attention, "segment_attention", _attention_variant("drop_past"), ATTN_PINS),
     "attention: keys used as values": (attention, "segment_attention", _attention_variant("keys_as_values"), ATTN_PINS),

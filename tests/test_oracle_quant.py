@@ -83,8 +83,11 @@ def _rne_int(fr):
 
 # 0x3F96 and 0x3FB4 hold x = m/2, whose float32 quotient rounds onto the tie 63.5:
 # they separate "round the quotient to float32, then to an integer" from rounding
-# the exact quotient.
-@pytest.mark.parametrize("m_bits", [0x3F80, 0x4080, 0x40A0, 0x42A0, 0x3A83, 0x0081, 0x3F96, 0x3FB4])
+# the exact quotient. At 0x3A8F the float32 scale lies above m/127, so x = m/2
+# divided by it gives 63 while x divided by the unrounded m/127 gives the tie
+# 63.5 and 64: it separates codes against the stored (float32) scale from codes
+# against the exact one.
+@pytest.mark.parametrize("m_bits", [0x3F80, 0x4080, 0x40A0, 0x42A0, 0x3A83, 0x0081, 0x3F96, 0x3FB4, 0x3A8F])
 def test_exhaustive_against_exact_rational(m_bits):    # Q5
     # all non-negative bf16 x <= m (and their negatives by symmetry of the code)
     m = float(formats.from_bf16_bits(np.array([m_bits], np.uint16))[0])

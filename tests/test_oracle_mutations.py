@@ -55,7 +55,8 @@ RING_PINS = [PG.test_window_is_last_capacity_frames, PG.test_append_larger_than_
              PG.test_evicted_then_retained_is_every_frame_in_order]
 SPARSE_PINS = [PS.test_all_blocks_selected_is_dense, PS.test_no_blocks_selected_is_segment_only,
                PS.test_selected_rows_only_matter, PS.test_planted_blocks_are_chosen,
-               PS.test_ties_go_to_lower_index_and_lists_ascend, PS.test_selection_invariances]
+               PS.test_ties_go_to_lower_index_and_lists_ascend, PS.test_selection_invariances,
+               PS.test_short_last_block_mean_is_over_its_own_rows]
 QKV_PINS = [PK.test_brute_force_projection, PK.test_identity_weights_give_rope_of_the_input,
             PK.test_rotation_preserves_pair_norms_and_values_are_unrotated]
 FORMAT_PINS = [PF.test_to_bf16_matches_torch_on_float32_patterns, PF.test_to_bf16_single_rounding_from_float64_brute_force]
@@ -232,6 +233,20 @@ class _RingSlotsFromOne(ring.RingModel):
         return {(f + 1) % self.capacity: (f, p) for f, p in self.frames}
 
 
+def _block_means_full_divisor(x, block):
+    """Short last block averaged over a full block's row count."""
+    x = np.asarray(x, np.float64)
+    nb = (x.shape[0] + block - 1) // block
+    return np.stack([x[b * block:(b + 1) * block].sum(axis=0) / block for b in range(nb)])
+
+
+def _positions_without_t0(t0, n_frames, grid_h, grid_w):
+    return _ORIG_POSITIONS(0, n_frames, grid_h, grid_w)
+
+
+_ORIG_POSITIONS = rope.video_positions
+
+
 # ---- format slip
 def _to_bf16_truncate(x):
     f = np.asarray(x, dtype=np.float64).astype(np.float32)
@@ -244,6 +259,7 @@ MUTANTS = {
     "rope: pairs as band halves": (rope, "rope3d", _rope_variant("halves"), ROPE_PINS),
     "rope: frequency exponent j/d": (rope, "angles", _angles_half_exponent, ROPE_PINS),
     "rope: h and w positions swapped": (rope, "video_positions", _positions_hw_swapped, ROPE_PINS),
+    "rope: frame positions from 0 instead of t0": (rope, "video_positions", _positions_without_t0, ROPE_PINS),
     "quant: scale absmax/128": (quant, "quantise", _quantise_variant(div=128.0), QUANT_PINS),
     "quant: ties away from zero": (quant, "quantise", _quantise_variant(rounding="away"), QUANT_PINS),
     "quant: quotient not rounded to fp32": (quant, "quantise", _quantise_variant(f32_quotient=False), QUANT_PINS),
@@ -258,6 +274,7 @@ MUTANTS = {
     "sparse: lowest scores selected": (sparse, "select_blocks", _select_variant("lowest"), SPARSE_PINS),
     "sparse: ties to the higher index": (sparse, "select_blocks", _select_variant("ties_high"), SPARSE_PINS),
     "sparse: block sums instead of means": (sparse, "block_means", _block_means_sum, SPARSE_PINS),
+    "sparse: short last block over a full count": (sparse, "block_means", _block_means_full_divisor, SPARSE_PINS),
     "sparse: short last block dropped": (sparse, "sparse_segment_attention", _sparse_attention_drops_last_partial,
                                           SPARSE_PINS),
     "qkv: RoPE applied to values": (qkv, "qkv_projection", _qkv_variant("rope_on_values"), QKV_PINS),

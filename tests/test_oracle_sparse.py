@@ -88,3 +88,16 @@ def test_selection_invariances():
     perm = np.concatenate([np.random.default_rng(19).permutation(np.arange(b * 128, min(1000, (b + 1) * 128)))
                            for b in range(8)])
     assert np.array_equal(base, sparse.select_blocks(q, kp[perm], 3))
+
+
+def test_short_last_block_mean_is_over_its_own_rows():
+    """A candidate block's score uses the plain mean of the rows it holds: the
+    short last block of a cache that is not a whole number of blocks averages
+    over its own rows (here 2 of 128), written out by hand."""
+    x = np.ones((130, 1, 2))
+    x[128] = [2.0, 4.0]
+    x[129] = [4.0, 8.0]
+    m = sparse.block_means(x, 128)
+    assert m.shape == (2, 1, 2)
+    assert np.array_equal(m[0], [[1.0, 1.0]])
+    assert np.array_equal(m[1], [[3.0, 6.0]])

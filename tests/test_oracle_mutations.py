@@ -93,6 +93,11 @@ def _angles_half_exponent(pos, width, theta=10000.0):
     return np.asarray(pos, dtype=np.float64)[:, None] * (theta ** (-1.0 * j / width))[None, :]
 
 
+def _angles_base_1000(pos, width, theta=10000.0):
+    j = np.arange(width // 2, dtype=np.float64)
+    return np.asarray(pos, dtype=np.float64)[:, None] * (1000.0 ** (-2.0 * j / width))[None, :]
+
+
 def _positions_hw_swapped(t0, n_frames, grid_h, grid_w):
     i = np.arange(n_frames * grid_h * grid_w, dtype=np.int64)
     return t0 + i // (grid_h * grid_w), i % grid_h, (i // grid_h) % grid_w
@@ -258,6 +263,7 @@ MUTANTS = {
     "rope: rotation sense reversed": (rope, "rope3d", _rope_variant("adjacent", swap_sin=True), ROPE_PINS),
     "rope: pairs as band halves": (rope, "rope3d", _rope_variant("halves"), ROPE_PINS),
     "rope: frequency exponent j/d": (rope, "angles", _angles_half_exponent, ROPE_PINS),
+    "rope: frequency base 1000 whatever theta": (rope, "angles", _angles_base_1000, ROPE_PINS),
     "rope: h and w positions swapped": (rope, "video_positions", _positions_hw_swapped, ROPE_PINS),
     "rope: frame positions from 0 instead of t0": (rope, "video_positions", _positions_without_t0, ROPE_PINS),
     "quant: scale absmax/128": (quant, "quantise", _quantise_variant(div=128.0), QUANT_PINS),

@@ -120,6 +120,30 @@ def _quantise_variant(div=127.0, rounding="even", f32_quotient=True, f32_scale=T
     return q
 
 
+def _quantise_scale_per_token(x):
+    """One scale per token across all heads (instead of per token and head)."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim < 2:
+        return quant_orig(x)
+    m = np.max(np.abs(x), axis=(-2, -1), keepdims=True)
+    s = (m / 127.0).astype(np.float32)
+    s64 = s.astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    r = (x / safe).astype(np.float32).astype(np.float64)
+    q = np.where(s64 > 0, np.clip(np.rint(r), -127, 127), 0.0)
+    return q.astype(np.int8), np.broadcast_to(s[..., 0], x.shape[:-1]).astype(np.float32)
+
+
+def _to_bf16_ties_away(x):
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x8000) & 0xFFFF0000).astype(np.uint32)
+    return u.view(np.float32).astype(np.float64)
+
+
+quant_orig = quant.quantise
+
+
 # ---- attention slips
 def _attention_variant(slip):
     orig = attention.segment_attention
@@ -270,6 +294,7 @@ MUTANTS = {
     "quant: ties away from zero": (quant, "quantise", _quantise_variant(rounding="away"), QUANT_PINS),
     "quant: quotient not rounded to fp32": (quant, "quantise", _quantise_variant(f32_quotient=False), QUANT_PINS),
     "quant: codes against the unrounded scale": (quant, "quantise", _quantise_variant(f32_scale=False), QUANT_PINS),
+    "quant: one scale per token across heads": (quant, "quantise", _quantise_scale_per_token, QUANT_PINS),
     "attention: scale dropped": (attention, "segment_attention", _attention_variant("no_scale"), ATTN_PINS),
     "attention: cached keys dropped": (attention, "segment_attention", _attention_variant("drop_past"), ATTN_PINS),
     "attention: keys used as values": (attention, "segment_attention", _attention_variant("keys_as_values"), ATTN_PINS),
@@ -289,6 +314,7 @@ MUTANTS = {
     "ring: window one frame short": (ring, "RingModel", _RingOneShort, RING_PINS),
     "ring: slots counted from one": (ring, "RingModel", _RingSlotsFromOne, RING_PINS),
     "formats: bf16 by truncation": (formats, "to_bf16", _to_bf16_truncate, FORMAT_PINS),
+    "formats: bf16 ties away from zero": (formats, "to_bf16", _to_bf16_ties_away, FORMAT_PINS),
 }
 
 

@@ -57,7 +57,7 @@ SPARSE_PINS = [PS.test_all_blocks_selected_is_dense, PS.test_no_blocks_selected_
                PS.test_selected_rows_only_matter, PS.test_planted_blocks_are_chosen,
                PS.test_ties_go_to_lower_index_and_lists_ascend, PS.test_selection_invariances,
                PS.test_short_last_block_mean_is_over_its_own_rows]
-QKV_PINS = [PK.test_brute_force_projection, PK.test_identity_weights_give_rope_of_the_input,
+QKV_PINS = [PK.test_brute_force_projection, PK.test_identity_weights_give_rope_of_the_input, PK.test_one_rounding_after_the_rotation,
             PK.test_rotation_preserves_pair_norms_and_values_are_unrotated]
 FORMAT_PINS = [PF.test_to_bf16_matches_torch_on_float32_patterns, PF.test_to_bf16_single_rounding_from_float64_brute_force]
 
@@ -232,6 +232,18 @@ def _qkv_variant(slip):
                 v = v.copy()
                 v[:n_video] = formats.to_bf16(qkv.rope3d_segment(v[:n_video], *args))
             return q, k, v
+        if slip == "round_before_rope":
+            # the product rounded to bf16 before the rotation as well (two roundings)
+            x64, w64 = np.asarray(x, np.float64), np.asarray(w, np.float64)
+            H, D = n_heads, head_dim
+            y = formats.to_bf16(x64 @ w64.T)
+            q, k, v = (y[:, i * H * D:(i + 1) * H * D].reshape(-1, H, D).copy() for i in range(3))
+            if rope is not None and n_video > 0:
+                r = dict(rope)
+                args = (r["t0"], r["n_frames"], r["grid_h"], r["grid_w"], r["d_t"], r["d_h"], r["d_w"])
+                q[:n_video] = qkv.rope3d_segment(q[:n_video], *args)
+                k[:n_video] = qkv.rope3d_segment(k[:n_video], *args)
+            return formats.to_bf16(q), formats.to_bf16(k), formats.to_bf16(v)
         # q and k channel blocks exchanged
         q, k, v = orig(x, w, n_heads, head_dim, n_video, rope)
         return k, q, v
@@ -310,6 +322,8 @@ MUTANTS = {
                                           SPARSE_PINS),
     "qkv: RoPE applied to values": (qkv, "qkv_projection", _qkv_variant("rope_on_values"), QKV_PINS),
     "qkv: q and k blocks exchanged": (qkv, "qkv_projection", _qkv_variant("qk_swapped"), QKV_PINS),
+    "qkv: rounded to bf16 before the rotation too": (qkv, "qkv_projection", _qkv_variant("round_before_rope"),
+                                                     QKV_PINS),
     "ring: evicts the newest frame": (ring, "RingModel", _RingKeepsOldest, RING_PINS),
     "ring: window one frame short": (ring, "RingModel", _RingOneShort, RING_PINS),
     "ring: slots counted from one": (ring, "RingModel", _RingSlotsFromOne, RING_PINS),

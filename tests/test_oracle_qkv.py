@@ -43,3 +43,18 @@ def test_rotation_preserves_pair_norms_and_values_are_unrotated():
     assert np.array_equal(v, v0) and np.array_equal(q[nv:], q0[nv:])
     pn = lambda t: np.sqrt(t[..., 0::2] ** 2 + t[..., 1::2] ** 2)
     assert np.max(np.abs(pn(q[:nv]) - pn(q0[:nv])) / (pn(q0[:nv]) + 1e-3)) < 2 ** -6
+
+
+def test_one_rounding_after_the_rotation():
+    # the rotated video-row q, k lie within half a bf16 ulp of the rotation of
+    # the exact product: the product is rounded once, after RoPE (a rounding
+    # before the rotation as well can land a full ulp away)
+    H, D, gh, gw, F = 1, 64, 4, 4, 2
+    nv = F * gh * gw
+    x, w = _bf((nv, 48), 6), _bf((3 * H * D, 48), 7, 0.15)
+    r = dict(t0=3, n_frames=F, grid_h=gh, grid_w=gw, d_t=16, d_h=24, d_w=24)
+    q, k, _ = qkv.qkv_projection(x, w, H, D, n_video=nv, rope=r)
+    y = x @ w.T
+    for got, blk in ((q, 0), (k, 1)):
+        exact = rope.rope3d_segment(y[:, blk * H * D:(blk + 1) * H * D].reshape(nv, H, D), 3, F, gh, gw, 16, 24, 24)
+        assert np.all(np.abs(got - exact) <= 0.5 * formats.bf16_ulp(got) * (1 + 1e-12))

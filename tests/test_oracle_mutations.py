@@ -43,7 +43,7 @@ ROPE_PINS = [PR.test_positions_match_explicit_loops, PR.test_pair_norms_preserve
              PR.test_zero_position_is_identity, PR.test_one_axis_is_complex_multiplication,
              PR.test_band_layout_unit_vectors, PR.test_relative_shift_invariance]
 QUANT_PINS = [PQ.test_roundtrip_within_half_step, PQ.test_special_cases, PQ.test_ties_round_to_even,
-              PQ.test_every_code_is_exact_in_bf16] + \
+              PQ.test_every_code_is_exact_in_bf16, PQ.test_dequantised_values_are_exact_products] + \
              [lambda m=m: PQ.test_exhaustive_against_exact_rational(m)
               for m in (0x3F80, 0x4080, 0x40A0, 0x42A0, 0x3A83, 0x0081, 0x3F96, 0x3FB4, 0x3A8F)]
 ATTN_PINS = [PA.test_probability_rows_sum_to_one, PA.test_ones_values_give_ones,
@@ -132,6 +132,10 @@ def _quantise_scale_per_token(x):
     r = (x / safe).astype(np.float32).astype(np.float64)
     q = np.where(s64 > 0, np.clip(np.rint(r), -127, 127), 0.0)
     return q.astype(np.int8), np.broadcast_to(s[..., 0], x.shape[:-1]).astype(np.float32)
+
+
+def _dequantise_to_bf16(q, s):
+    return formats.to_bf16(np.asarray(q, dtype=np.float64) * np.asarray(s, dtype=np.float64)[..., None])
 
 
 def _to_bf16_ties_away(x):
@@ -307,6 +311,7 @@ MUTANTS = {
     "quant: quotient not rounded to fp32": (quant, "quantise", _quantise_variant(f32_quotient=False), QUANT_PINS),
     "quant: codes against the unrounded scale": (quant, "quantise", _quantise_variant(f32_scale=False), QUANT_PINS),
     "quant: one scale per token across heads": (quant, "quantise", _quantise_scale_per_token, QUANT_PINS),
+    "quant: dequantised values rounded to bf16": (quant, "dequantise", _dequantise_to_bf16, QUANT_PINS),
     "attention: scale dropped": (attention, "segment_attention", _attention_variant("no_scale"), ATTN_PINS),
     "attention: cached keys dropped": (attention, "segment_attention", _attention_variant("drop_past"), ATTN_PINS),
     "attention: keys used as values": (attention, "segment_attention", _attention_variant("keys_as_values"), ATTN_PINS),

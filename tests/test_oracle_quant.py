@@ -108,3 +108,14 @@ def test_exhaustive_against_exact_rational(m_bits):    # Q5
             frac = Fraction(float(xi)) * 127 / Fraction(m)
             assert abs(frac - (Fraction(int(qi) + alt, 2))) < Fraction(1, 2 ** 12)
     assert alt_disagree <= len(xs) // 100
+
+
+def test_dequantised_values_are_exact_products():
+    # the attention reference sees code * scale exactly (no bf16 rounding): with
+    # the float32 scale of 0.1, code 3 dequantises to 3 * 0.100000001490116...
+    s = np.array([np.float32(0.1)], np.float32)
+    q = np.array([[3, -127, 1]], np.int8)
+    x = quant.dequantise(q, s)
+    s64 = float(np.float32(0.1))          # 0.100000001490116119384765625
+    assert x[0, 0] == 0.300000004470348358154296875 == 3 * s64
+    assert x[0, 1] == -12.7000001892447471618652343750 and x[0, 2] == s64

@@ -88,6 +88,13 @@ def _rope_variant(pair, swap_sin=False):
     return rope3d
 
 
+_ORIG_ROPE3D = rope.rope3d
+
+
+def _rope_ignores_sign(x, t, h, w, d_t, d_h, d_w, theta=10000.0, sign=1.0):
+    return _ORIG_ROPE3D(x, t, h, w, d_t, d_h, d_w, theta)
+
+
 def _angles_half_exponent(pos, width, theta=10000.0):
     j = np.arange(width // 2, dtype=np.float64)
     return np.asarray(pos, dtype=np.float64)[:, None] * (theta ** (-1.0 * j / width))[None, :]
@@ -303,6 +310,7 @@ MUTANTS = {
     "rope: rotation sense reversed": (rope, "rope3d", _rope_variant("adjacent", swap_sin=True), ROPE_PINS),
     "rope: pairs as band halves": (rope, "rope3d", _rope_variant("halves"), ROPE_PINS),
     "rope: frequency exponent j/d": (rope, "angles", _angles_half_exponent, ROPE_PINS),
+    "rope: inverse rotation not inverted": (rope, "rope3d", _rope_ignores_sign, ROPE_PINS),
     "rope: frequency base 1000 whatever theta": (rope, "angles", _angles_base_1000, ROPE_PINS),
     "rope: h and w positions swapped": (rope, "video_positions", _positions_hw_swapped, ROPE_PINS),
     "rope: frame positions from 0 instead of t0": (rope, "video_positions", _positions_without_t0, ROPE_PINS),

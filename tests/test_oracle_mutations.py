@@ -48,7 +48,8 @@ QUANT_PINS = [PQ.test_roundtrip_within_half_step, PQ.test_special_cases, PQ.test
               for m in (0x3F80, 0x4080, 0x40A0, 0x42A0, 0x3A83, 0x0081, 0x3F96, 0x3FB4, 0x3A8F)]
 ATTN_PINS = [PA.test_probability_rows_sum_to_one, PA.test_ones_values_give_ones,
              PA.test_constant_keys_give_mean_and_frame_histogram, PA.test_single_key_and_dominant_logit,
-             PA.test_key_permutation_invariance, PA.test_brute_force_tiny] + \
+             PA.test_key_permutation_invariance, PA.test_brute_force_tiny, PA.test_brute_force_tiny_workload_rows,
+             PA.test_rows_helper_matches_full, PA.test_block_causal_row_subset, PA.test_window_changes_result] + \
             [lambda s=s: PA.test_split_merge_equals_unsplit(s) for s in (2, 3, 7)] + \
             [lambda i=i, w=w: PA.test_cached_equals_full_block_causal(i, w) for i in (False, True) for w in (None, 4, 3)]
 RING_PINS = [PG.test_window_is_last_capacity_frames, PG.test_append_larger_than_capacity_keeps_tail,
@@ -171,6 +172,14 @@ def _attention_variant(slip):
             return (res[0], res[1] / math.log(2.0)) + tuple(res[2:])
         return res
     return seg
+
+
+_ORIG_ROWS = attention.segment_attention_rows
+
+
+def _rows_heads_misread(q_rows, row_heads, k, v, scale):
+    """Every sampled row attended with head 0's keys and values."""
+    return _ORIG_ROWS(q_rows, np.zeros_like(np.asarray(row_heads)), k, v, scale)
 
 
 def _softmax_no_normalisation(s):
@@ -324,6 +333,7 @@ MUTANTS = {
     "attention: cached keys dropped": (attention, "segment_attention", _attention_variant("drop_past"), ATTN_PINS),
     "attention: keys used as values": (attention, "segment_attention", _attention_variant("keys_as_values"), ATTN_PINS),
     "attention: log-sum-exp in log2 units": (attention, "segment_attention", _attention_variant("lse_log2"), ATTN_PINS),
+    "attention: sampled rows read with head 0": (attention, "segment_attention_rows", _rows_heads_misread, ATTN_PINS),
     "attention: softmax not normalised": (attention, "_softmax_rows", _softmax_no_normalisation, ATTN_PINS),
     "attention: split weights not normalised": (attention, "split_attention", _split_unnormalised_weights, ATTN_PINS),
     "attention: window mask off by one": (attention, "block_causal_full", _block_causal_window_off_by_one(), ATTN_PINS),

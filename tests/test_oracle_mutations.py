@@ -182,6 +182,15 @@ def _rows_heads_misread(q_rows, row_heads, k, v, scale):
     return _ORIG_ROWS(q_rows, np.zeros_like(np.asarray(row_heads)), k, v, scale)
 
 
+_ORIG_BCF = attention.block_causal_full
+
+
+def _block_causal_raw_past(segments, *args, **kwargs):
+    """Earlier segments' video keys/values as written, not as the cache holds them."""
+    segs = [{k: v for k, v in sg.items() if k not in ("k_past", "v_past")} for sg in segments]
+    return _ORIG_BCF(segs, *args, **kwargs)
+
+
 def _softmax_no_normalisation(s):
     m = np.max(s, axis=-1, keepdims=True)
     p = np.exp(s - m)
@@ -334,6 +343,8 @@ MUTANTS = {
     "attention: keys used as values": (attention, "segment_attention", _attention_variant("keys_as_values"), ATTN_PINS),
     "attention: log-sum-exp in log2 units": (attention, "segment_attention", _attention_variant("lse_log2"), ATTN_PINS),
     "attention: sampled rows read with head 0": (attention, "segment_attention_rows", _rows_heads_misread, ATTN_PINS),
+    "attention: earlier segments' keys raw, not as cached": (attention, "block_causal_full", _block_causal_raw_past,
+                                                             ATTN_PINS),
     "attention: softmax not normalised": (attention, "_softmax_rows", _softmax_no_normalisation, ATTN_PINS),
     "attention: split weights not normalised": (attention, "split_attention", _split_unnormalised_weights, ATTN_PINS),
     "attention: window mask off by one": (attention, "block_causal_full", _block_causal_window_off_by_one(), ATTN_PINS),

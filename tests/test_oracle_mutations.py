@@ -57,7 +57,7 @@ RING_PINS = [PG.test_window_is_last_capacity_frames, PG.test_append_larger_than_
 SPARSE_PINS = [PS.test_all_blocks_selected_is_dense, PS.test_no_blocks_selected_is_segment_only,
                PS.test_selected_rows_only_matter, PS.test_planted_blocks_are_chosen,
                PS.test_ties_go_to_lower_index_and_lists_ascend, PS.test_selection_invariances,
-               PS.test_short_last_block_mean_is_over_its_own_rows]
+               PS.test_short_last_block_mean_is_over_its_own_rows, PS.test_each_head_uses_its_own_list]
 QKV_PINS = [PK.test_brute_force_projection, PK.test_identity_weights_give_rope_of_the_input, PK.test_one_rounding_after_the_rotation,
             PK.test_rotation_preserves_pair_norms_and_values_are_unrotated]
 FORMAT_PINS = [PF.test_to_bf16_matches_torch_on_float32_patterns, PF.test_to_bf16_single_rounding_from_float64_brute_force]
@@ -317,6 +317,15 @@ def _positions_without_t0(t0, n_frames, grid_h, grid_w):
 _ORIG_POSITIONS = rope.video_positions
 
 
+_ORIG_SPARSE_ATTN = sparse.sparse_segment_attention
+
+
+def _sparse_lists_of_head0(q, k_cur, v_cur, k_past, v_past, lists, scale):
+    """Every head attends to head 0's block list."""
+    lists = np.asarray(lists)
+    return _ORIG_SPARSE_ATTN(q, k_cur, v_cur, k_past, v_past, np.broadcast_to(lists[:1], lists.shape), scale)
+
+
 # ---- format slip
 def _to_bf16_truncate(x):
     f = np.asarray(x, dtype=np.float64).astype(np.float32)
@@ -352,6 +361,8 @@ MUTANTS = {
     "sparse: ties to the higher index": (sparse, "select_blocks", _select_variant("ties_high"), SPARSE_PINS),
     "sparse: block sums instead of means": (sparse, "block_means", _block_means_sum, SPARSE_PINS),
     "sparse: short last block over a full count": (sparse, "block_means", _block_means_full_divisor, SPARSE_PINS),
+    "sparse: every head takes head 0's list": (sparse, "sparse_segment_attention", _sparse_lists_of_head0,
+                                               SPARSE_PINS),
     "sparse: short last block dropped": (sparse, "sparse_segment_attention", _sparse_attention_drops_last_partial,
                                           SPARSE_PINS),
     "qkv: RoPE applied to values": (qkv, "qkv_projection", _qkv_variant("rope_on_values"), QKV_PINS),

@@ -101,3 +101,21 @@ def test_short_last_block_mean_is_over_its_own_rows():
     assert m.shape == (2, 1, 2)
     assert np.array_equal(m[0], [[1.0, 1.0]])
     assert np.array_equal(m[1], [[3.0, 6.0]])
+
+
+def test_each_head_uses_its_own_list():
+    # two heads with different lists and two query blocks: every (query block,
+    # head) output equals the dense cached attention of that head against the
+    # rows its own list names (and a query block uses its own list)
+    q, kc, vc = _r((300, 2, 64), 31), _r((20, 2, 64), 32), _r((20, 2, 64), 33)
+    kp, vp = _r((384, 2, 64), 34), _r((384, 2, 64), 35)
+    lists = np.array([[[0], [2]], [[1], [0]]], np.int32)          # [H, query block, n_select]
+    out, lse = sparse.sparse_segment_attention(q, kc, vc, kp, vp, lists, 0.125)
+    for h in range(2):
+        for b, r in enumerate((slice(0, 256), slice(256, 300))):
+            c = lists[h, b, 0]
+            rows = slice(c * 128, (c + 1) * 128)
+            a, la = attention.segment_attention(q[r, h:h + 1], kc[:, h:h + 1], vc[:, h:h + 1],
+                                                kp[rows, h:h + 1], vp[rows, h:h + 1], 0.125)
+            assert np.max(np.abs(out[r, h] - a[:, 0])) < 1e-13
+            assert np.max(np.abs(lse[h, r] - la[0])) < 1e-12

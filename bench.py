@@ -117,6 +117,16 @@ def layer_step_bench(args):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the graphics clock under this load: the same attention launches repeated
+    # for a few seconds while amd-smi is sampled (the timed steps above last
+    # well under the sampling period)
+    clk = ClockSampler()
+    with clk:
+        t_end = time.perf_counter() + 3.0
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
+            torch.cuda.synchronize()
     rope_ms = [e[0].elapsed_time(e[1]) for e in ev]
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
     app_ms = [e[2].elapsed_time(e[3]) for e in ev]
@@ -129,12 +139,110 @@ def layer_step_bench(args):
         attn_ms_p90=statistics.quantiles(attn_ms, n=10)[-1],
         rope_ms_mean=statistics.mean(rope_ms),
         append_ms_mean=statistics.mean(app_ms),
+        sclk_mhz=clk.mhz(),
+        sclk_samples=len(clk.samples),
+        sclk_raw=None if clk.samples else clk.raw,
         rope_bytes=2 * 2 * wl.n_video * H * D * 2,             # read + write Q and K video rows
         append_bytes=2 * wl.n_video * H * D * 2 * 2,           # bf16 window: read K,V + write K,V
     )
     log(f"[bench] layer step: {res['ms_per_step']:.3f} ms/step, attention {res['attn_ms_mean']:.3f} ms "
         f"({flop / res['attn_ms_mean'] / 1e9:.1f} TFLOP/s)")
     return wl, res
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock with amd-smi in a background thread
+    while a timed region runs (a child process per sample; the GPU work is
+    not touched). ``mhz()`` is the median of the samples, or None when the
+    tool gives no reading."""
+
+    def __init__(self, period_s=0.2):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self.raw = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _read(self):
+        import re
+        import subprocess
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True, text=True,
+                               timeout=10)
+        except Exception as e:
+            self.raw = self.raw or f"amd-smi failed: {e}"
+            return None
+        if self.raw is None:
+            self.raw = r.stdout[:4000]
+        # the graphics clock's current value: the first "gfx" entry's clk value
+        m = re.search(r'"gfx_0"\s*:\s*\{[^{}]*?"clk"\s*:\s*\{\s*"value"\s*:\s*(\d+)', r.stdout)
+        if not m:
+            m = re.search(r'"gfx[^"]*"\s*:\s*\{[^{}]*?"clk"\s*:\s*(\d+)', r.stdout)
+        return int(m.group(1)) if m else None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v:
+                self.samples.append(v)
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def mhz(self):
+        return statistics.median(self.samples) if self.samples else None
+
+
+def layer_int8_bench(reps=20):
+    """The single-layer shape with an INT8 window (16x128 heads, 18 frames of
+    24x40, 4 outlier key channels per head at 20x): the attention launch and the
+    quantise-append of the 8-frame segment, each timed on its own with HIP
+    events."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["layer_int8"]
+    H, D, F = wl.n_heads, wl.head_dim, wl.seg_frames
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, True)
+    kb, vb = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    out = torch.empty_like(q)
+    ws = nomas.workspace_for(cache, wl.n_video, wl.n_text)
+    attn = lambda: nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
+    app = lambda: cache.nomas_kvcache_append(k, v, F)
+    res = {}
+    for name, fn in (("attention", attn), ("append", app)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        res[name] = statistics.median(ms)
+    flop = wl.attention_flop()
+    # read K, V bf16 + write K, V codes + one fp32 scale per (token, head) each
+    app_bytes = 2 * wl.n_video * H * D * 2 + 2 * wl.n_video * H * D + 2 * wl.n_video * H * 4
+    log(f"[bench] INT8 layer: attention {res['attention']:.3f} ms ({flop / res['attention'] / 1e9:.1f} TFLOP/s), "
+        f"quantise-append {res['append'] * 1e3:.1f} us ({app_bytes / res['append'] / 1e6:.0f} GB/s)")
+    return dict(int8_attention_ms=round(res["attention"], 4),
+                int8_attention_tflops=round(flop / res["attention"] / 1e9, 1),
+                int8_attention_pct_mfma_peak=round(100 * flop / res["attention"] / 1e9 / PEAK_BF16_TFLOPS, 2),
+                int8_append_us=round(res["append"] * 1e3, 2),
+                int8_append_gbps=round(app_bytes / res["append"] / 1e6, 1),
+                int8_append_bytes=app_bytes)
 
 
 def attention_cold_bench(reps=20):
@@ -433,11 +541,12 @@ def cpu_baseline(rows_per_head):
     import numpy as np
     from oracle import attention
     from segment_autoregressive_dit_amd import synth
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = cores
     wl = synth.WORKLOADS["layer_bf16"]
     q, k, v = (synth.bf16_bits_to_f64(t) for t in synth.current_qkv(wl))
     kp, vp = (synth.bf16_bits_to_f64(t) for t in synth.prefill_kv(wl))
@@ -447,9 +556,17 @@ def cpu_baseline(rows_per_head):
     dt = time.perf_counter() - t0
     flop = 4 * len(rows) * wl.n_k * wl.head_dim * wl.n_heads
     log(f"[bench] cpu oracle: {len(rows)} rows x {wl.n_heads} heads in {dt:.2f} s")
-    out = dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+    full_call_s = dt * wl.n_q / len(rows)
+    dn = synth.WORKLOADS["denoise_int8"]
+    calls = dn.n_layers * dn.n_steps * dn.n_turns
+    out = dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=cores, blas_threads=threads, kind="oracle",
                sample=f"{len(rows)} of {wl.n_q} query rows per head, all {wl.n_heads} heads, all {wl.n_k} keys "
-                      f"({flop / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy)")
+                      f"({flop / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy)",
+               # the denoise sweep's attention calls have the layer call's shape
+               # (its INT8 window enters the oracle as float64 values)
+               denoise_sweep_s=round(full_call_s * calls, 1),
+               denoise_sweep_kind=f"extrapolation: one layer call ({full_call_s:.2f} s) x {calls} calls "
+                                  f"({dn.n_layers} layers x {dn.n_steps} steps x {dn.n_turns} turns), not a run")
     # the same oracle on one thread, on a sample cut by the thread count
     try:
         from threadpoolctl import threadpool_limits
@@ -494,11 +611,15 @@ def main():
 
     wl, r = layer_step_bench(args)
     value = r["flop"] / (r["ms_per_step"] * 1e-3) / 1e12
-    attn_tflops = r["flop"] / (r["attn_ms_mean"] * 1e-3) / 1e12
+    # roofline: the median attention launch of the timed steps
+    attn_tflops = r["flop"] / (r["attn_ms_median"] * 1e-3) / 1e12
     extra = dict(
-        attention_ms=round(r["attn_ms_mean"], 4),
+        attention_ms=round(r["attn_ms_median"], 4),
+        attention_ms_mean=round(r["attn_ms_mean"], 4),
         attention_tflops=round(attn_tflops, 1),
         attention_pct_mfma_peak=round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        sclk_mhz_under_attention=r["sclk_mhz"],
+        sclk_samples=r["sclk_samples"],
         rope_us=round(r["rope_ms_mean"] * 1e3, 2),
         rope_gbps=round(r["rope_bytes"] / (r["rope_ms_mean"] * 1e-3) / 1e9, 1),
         append_us=round(r["append_ms_mean"] * 1e3, 2),
@@ -506,7 +627,10 @@ def main():
         attention_ms_p10=round(r["attn_ms_p10"], 4),
         attention_ms_p90=round(r["attn_ms_p90"], 4),
     )
+    if r["sclk_raw"] is not None:
+        extra["sclk_raw"] = r["sclk_raw"][:400]
     if not args.headline_only:
+        extra.update(layer_int8_bench())
         extra.update(attention_cold_bench())
         extra.update(long_history_bench())
     if not args.no_denoise and not args.headline_only:

@@ -862,14 +862,18 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     if (pn < tiles_total_b && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
   }
 
-  // ---- epilogue
+  // ---- epilogue. A sparse block whose list leaves its split no key tile (its
+  // last candidate block is short, so it has fewer tiles than the split count
+  // was planned for) has l = 0: it writes O = 0 and lse = -inf, which the merge
+  // weighs by exp(-inf) = 0. Any block that ran a tile has l >= 1 (the tile's
+  // largest key enters with probability 1).
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = lacc[qb][0];
-    const float inv = 1.0f / l;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
     const int row = q_row0 + (wave * QB + qb) * 16 + i16;
     if (row >= q_end) continue;
-    const float lse = (m_ref[qb] + log2f(l)) * kLn2;
+    const float lse = l > 0.f ? (m_ref[qb] + log2f(l)) * kLn2 : -INFINITY;
     if (!a.part_o) {
       uint16_t* dst = a.out + (int64_t)row * a.ld_out + (int64_t)h * D + 4 * G;
 #pragma unroll
@@ -903,6 +907,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < S; ++s) {
+    // an empty split (lse = -inf, O = 0) gets weight 0; m is finite because
+    // some split of every row has keys
     const int64_t pr = ((int64_t)s * H + h) * n_q + row;
     const float w = expf(part_lse[pr] - m);
     wsum += w;

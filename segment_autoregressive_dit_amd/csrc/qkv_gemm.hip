@@ -214,8 +214,12 @@ __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmAr
   }
 
   // ---- epilogue: RoPE on query/key channels of video rows, one bf16 rounding.
-  // The block's channels lie in one of query/key/value; the angles of a token's
-  // two pairs are one 16-byte load, all of a token column issued at once.
+  // A block may straddle the key/value boundary 2*H*D (head dim 64 with an odd
+  // head count), so the rotation is decided per 4-channel group; a group never
+  // straddles it (4-aligned groups, boundary a multiple of 128). The angles of a
+  // token's two pairs are one 16-byte load, all of a token column issued at
+  // once (also for value channels of such a block: the table index stays in
+  // range, the values go unused).
   const int D = a.head_dim, P = D / 2;
   const bool rot_block = a.table && ch0 < 2 * a.hd;
 #pragma unroll
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmAr
       const int ch = ch0 + wch + 16 * i + 4 * G;     // channels ch .. ch+3
       if (ch >= a.n_ch) continue;
       f32x4 v = acc[i][j];
-      if (rot) {
+      if (rot && ch < 2 * a.hd) {
         const float u0 = v[0], w0 = v[1], u1 = v[2], w1 = v[3];
         v[0] = fmaf(u0, cs[i][0], -w0 * cs[i][1]);
         v[1] = fmaf(u0, cs[i][1], w0 * cs[i][0]);

@@ -108,6 +108,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(t, stream):
+    """Mark a temporary allocated here as in use by ``stream`` when the caller
+    names a stream other than the current one, so that the caching allocator
+    does not hand its memory out again before the library's kernels on that
+    stream are done with it."""
+    if stream is not None and t is not None:
+        t.record_stream(stream)
+    return t
+
+
 def _rows_view(t, name, heads, head_dim):
     """(pointer, row stride) of a bf16 device tensor laid out [rows, ...heads*head_dim]."""
     if t.dtype != torch.bfloat16 or not t.is_cuda:
@@ -284,12 +294,13 @@ def nomas_sparse_select(q, n_q, cache, n_select, block_list=None, workspace=None
         raise ValueError("q holds fewer than n_q rows")
     nqb = (n_q + NOMAS_SPARSE_QUERY_BLOCK - 1) // NOMAS_SPARSE_QUERY_BLOCK
     if block_list is None:
-        block_list = torch.empty((H, nqb, max(n_select, 1)), dtype=torch.int32, device=q.device)[:, :, :n_select]
+        block_list = _on_stream(torch.empty((H, nqb, max(n_select, 1)), dtype=torch.int32, device=q.device),
+                                stream)[:, :, :n_select]
     if block_list.dtype != torch.int32 or not block_list.is_contiguous() or block_list.numel() < H * nqb * n_select:
         raise ValueError("block_list must be a contiguous int32 tensor of n_heads*n_qblocks*n_select elements")
     if workspace is None:
         nb = lib().nomas_sparse_select_workspace_bytes(n_q, cache.n_cached, H, D)
-        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        workspace = _on_stream(torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device), stream)
     _check(lib().nomas_sparse_select(qp, ld, n_q, ctypes.byref(d), n_select, ctypes.c_void_p(block_list.data_ptr()),
                                      ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
     return block_list
@@ -309,7 +320,7 @@ def _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, block_list, out,
         if t.shape[0] < n_q:
             raise ValueError(f"{name} holds fewer than n_video + n_text rows")
     if out is None:
-        out = torch.empty((n_q, H, D), dtype=torch.bfloat16, device=q.device)
+        out = _on_stream(torch.empty((n_q, H, D), dtype=torch.bfloat16, device=q.device), stream)
     op, ldo = _rows_view(out, "out", H, D)
     if out.shape[0] < n_q:
         raise ValueError("out holds fewer than n_video + n_text rows")
@@ -321,7 +332,7 @@ def _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, block_list, out,
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if block_list is None:
         if workspace is None:
-            workspace = workspace_for(cache, n_video, n_text, n_splits, q.device)
+            workspace = _on_stream(workspace_for(cache, n_video, n_text, n_splits, q.device), stream)
         _check(lib().nomas_segment_attention(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d), op, ldo, lp, scale,
                                              n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                              _stream(stream)))
@@ -330,11 +341,12 @@ def _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, block_list, out,
     if block_list.dtype != torch.int32 or block_list.dim() != 3 or block_list.shape[:2] != (H, nqb):
         raise ValueError(f"block_list must be int32 [{H}, {nqb}, n_select]")
     n_select = block_list.shape[2]
-    block_list = block_list.contiguous()
+    if not block_list.is_contiguous():
+        block_list = _on_stream(block_list.contiguous(), stream)
     if workspace is None:
         nb = nomas_segment_attention_workspace_bytes(n_video, n_text, n_select * NOMAS_SPARSE_KEY_BLOCK, H, D,
                                                      d.kv_dtype, n_splits)
-        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        workspace = _on_stream(torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device), stream)
     _check(lib().nomas_segment_attention_sparse(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d),
                                                 ctypes.c_void_p(block_list.data_ptr()), n_select, op, ldo, lp, scale,
                                                 n_splits, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
@@ -374,7 +386,7 @@ def nomas_block_causal_attention(q, k, v, segments, tokens_per_frame, window_fra
         if t.shape[0] < n_rows:
             raise ValueError(f"{name} holds fewer rows than the segments")
     if out is None:
-        out = torch.empty((n_rows, H, D), dtype=torch.bfloat16, device=q.device)
+        out = _on_stream(torch.empty((n_rows, H, D), dtype=torch.bfloat16, device=q.device), stream)
     op, ldo = _rows_view(out, "out", H, D)
     if out.shape[0] < n_rows:
         raise ValueError("out holds fewer rows than the segments")
@@ -385,7 +397,7 @@ def nomas_block_causal_attention(q, k, v, segments, tokens_per_frame, window_fra
         lp = ctypes.c_void_p(lse.data_ptr())
     if workspace is None:
         nb = nomas_block_causal_attention_workspace_bytes(segments, tokens_per_frame, H, D)
-        workspace = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+        workspace = _on_stream(torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device), stream)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     _check(lib().nomas_block_causal_attention(qp, kp, vp, ld, segs, len(segments), tokens_per_frame, window_frames,
                                               H, D, op, ldo, lp, scale, ctypes.c_void_p(workspace.data_ptr()),
@@ -401,7 +413,7 @@ def nomas_rope3d_table(head_dim, t0, n_frames, grid_h, grid_w, band, theta=10000
     if n == 0:
         return None
     if table is None:
-        table = torch.empty((n, head_dim // 2, 2), dtype=torch.float32, device="cuda")
+        table = _on_stream(torch.empty((n, head_dim // 2, 2), dtype=torch.float32, device="cuda"), stream)
     if table.dtype != torch.float32 or not table.is_cuda or not table.is_contiguous() or table.numel() < n * head_dim:
         raise ValueError("table must be a contiguous float32 CUDA tensor of n_rows*head_dim elements")
     d_t, d_h, d_w = band
@@ -421,7 +433,7 @@ def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qk
     if w.shape[0] != n_ch or w.shape[1] != hidden:
         raise ValueError(f"w must be [{n_ch}, {hidden}]")
     if qkv is None:
-        qkv = torch.empty((n, n_ch), dtype=torch.bfloat16, device=x.device)
+        qkv = _on_stream(torch.empty((n, n_ch), dtype=torch.bfloat16, device=x.device), stream)
     if qkv.dtype != torch.bfloat16 or qkv.dim() != 2 or qkv.stride(1) != 1 or qkv.shape[0] < n or qkv.shape[1] < n_ch:
         raise ValueError("qkv must be a 2-D bfloat16 tensor of at least [n, 3*H*D] with unit inner stride")
     tp = None

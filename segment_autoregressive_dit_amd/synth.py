@@ -102,6 +102,21 @@ def _round_bf16_bits(x32):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def device_normal_bf16(shape, wid, layer, turn, tid, device="cuda"):
+    """bf16 CUDA tensor of N(0, 1) float32 draws rounded to nearest even, from
+    torch's device generator seeded by (wid, layer, turn, tid).
+
+    For workloads too large to draw on the host in a test's time (the 54-layer
+    sweep draws about 12 billion values); the oracle reads the same values back
+    from the tensor. Same role as ``normal_bf16``: numbers only, no arithmetic of
+    the method."""
+    import torch
+    seed = int(np.random.SeedSequence([int(wid), int(layer), int(turn), int(tid)]).generate_state(1, np.uint64)[0])
+    g = torch.Generator(device=device)
+    g.manual_seed(seed >> 1)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 def outlier_channels(wl, layer=0):
     """[n_heads, k_outliers] channel indices scaled by 20 in every K row."""
     rng = rng_for(wl.wid, layer, 0, 5)

@@ -185,6 +185,27 @@ def test_workspace_and_split_planning():
     assert L.nomas_segment_attention_splits(10, 0, 0, 1, 64, 7, 0) == -1
 
 
+def test_sparse_split_plan_can_leave_a_split_without_tiles():
+    """The sparse call plans its splits for n_select * 128 listed rows, while a
+    block whose list ends in the short last candidate block has fewer key tiles.
+    A block's split s covers tiles [s*T/S, (s+1)*T/S) of its T tiles; with
+    64-key tiles (INT8 at head dim 128, or head dim 64) and one listed 20-row
+    block, the library plans S = 3 but the block has T = 2 tiles (1 cache + 1
+    current), so split 0 is empty. The kernel writes such a split as O = 0,
+    lse = -inf, which the merge weighs by 0 (GPU regression:
+    test_gpu_sparse.py::test_split_without_key_tiles)."""
+    L = nomas.lib()
+    for D, dt, key_tile in ((128, nomas.NOMAS_KV_INT8, 64), (64, nomas.NOMAS_KV_BF16, 64),
+                            (64, nomas.NOMAS_KV_INT8, 64)):
+        S = L.nomas_segment_attention_splits(0, 16, 128, 2, D, dt, 3)
+        assert S == 3
+        T = -(-20 // key_tile) + -(-16 // key_tile)
+        ranges = [(s * T // S, (s + 1) * T // S) for s in range(S)]
+        assert ranges[0] == (0, 0) and sum(b - a for a, b in ranges) == T
+    # bf16 at head dim 128 (128-key tiles) plans exactly the block's 2 tiles
+    assert L.nomas_segment_attention_splits(0, 16, 128, 2, 128, nomas.NOMAS_KV_BF16, 3) == 2
+
+
 def test_block_causal_rejects_before_launch():
     L = nomas.lib()
     segs = nomas._segments([(48, 16, 0), (48, 16, 2)])

@@ -41,7 +41,17 @@ def test_traffic_comes_from_a_matching_summary_only(tmp_path):
     bench = _bench_module()
     summary = json.load(open(bench.PMC_SUMMARY))
     assert summary["source"] == "attention.hip"
-    # the committed summary was taken from the committed kernel
+    # the figure is reported exactly when the summary was taken from the kernel
+    # as it stands (otherwise null until the counters are taken again)
+    if summary["source_digest"] == source_digest(bench.ATTN_SRC):
+        assert bench.traffic_per_launch() == summary["hbm_bytes_per_launch"]
+    else:
+        assert bench.traffic_per_launch() is None
+    # a summary of this very code yields its figure
+    same = dict(summary, source_digest=source_digest(bench.ATTN_SRC))
+    p0 = tmp_path / "same.json"
+    p0.write_text(json.dumps(same))
+    bench.PMC_SUMMARY = str(p0)
     assert bench.traffic_per_launch() == summary["hbm_bytes_per_launch"]
     # a summary of other code yields no figure
     other = dict(summary, source_digest="0" * 64)

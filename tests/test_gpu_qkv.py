@@ -57,6 +57,14 @@ def test_small_ragged():
     assert np.mean(diff) < 2 ** -9 * np.mean(np.abs(ref)) + 1e-6
 
 
+@pytest.mark.parametrize("H", [1, 3])
+def test_odd_heads_key_value_boundary_inside_a_block(H):
+    # head dim 64 with an odd head count: 2*H*64 is not a multiple of the
+    # 256-channel block, so one block holds both key and value channels; only
+    # the key channels may be rotated
+    _run(H, 64, 128, 1, 4, 6, 9, 2, (16, 24, 24), seed=5 + H)
+
+
 def test_mid_head128():
     # 4 heads of 128, hidden 512, 2 frames of 12x20 + 220 text rows
     _run(4, 128, 512, 2, 12, 20, 220, 18, (32, 48, 48), seed=1)

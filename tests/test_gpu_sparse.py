@@ -168,3 +168,26 @@ def test_layer_select_then_attend_sampled_rows():
     for r in rows:
         ref, _ = sparse.sparse_segment_attention(xq[r:r + 1], xk, xv, kp, vp, L[:, r // 256:r // 256 + 1], 1 / math.sqrt(D))
         _check(got[r:r + 1], ref, f"row {r}")
+
+
+@pytest.mark.parametrize("splits", [2, 3])
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_without_key_tiles(D, int8, splits):
+    """A list whose only block is the short last candidate (one 20-row frame):
+    the split count is planned for 128 listed rows, so with 64-key tiles (INT8,
+    or head dim 64) a block has fewer key tiles than splits and one split gets
+    none. That split must count for nothing in the merge (it once wrote NaN)."""
+    H, tpf, nv, nt = 2, 20, 0, 16
+    (q, k, v), cache, x, kp, vp = _setup(H, D, tpf, 1, nv, nt, int8, seed=7)
+    lists = np.zeros((H, 1, 1), np.int32)
+    say(f"sparse split without tiles: D={D} int8={int8} splits={splits}")
+    lse = torch.empty(H * (nv + nt), dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention_sparse(q, k, v, nv, nt, cache, torch.from_numpy(lists).cuda(), lse=lse,
+                                               n_splits=splits)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    assert np.all(np.isfinite(got)), "non-finite output from an empty split"
+    ref, ref_lse = sparse.sparse_segment_attention(x[0], x[1], x[2], kp, vp, lists, 1 / math.sqrt(D))
+    _check(got, ref, "split without key tiles")
+    assert np.max(np.abs(lse.cpu().numpy().reshape(H, -1) - ref_lse)) <= LSE_TOL

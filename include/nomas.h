@@ -23,6 +23,8 @@
  *   - The caller owns all memory. The library never allocates, frees or
  *     synchronises; every compute call enqueues kernels on `stream` (a
  *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *     (One exception: nomas_segment_attention_noalloc uses a scratch array
+ *     the library itself holds, for callers that cannot allocate.)
  *   - Every call returns a nomas_status. All arguments are checked on the host
  *     before anything is enqueued: on an error nothing is enqueued, the cache
  *     descriptor is unchanged, and nomas_last_error() describes the problem.
@@ -234,6 +236,27 @@ int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const 
                                 const nomas_kvcache* c, uint16_t* out, int64_t ld_out, float* lse,
                                 float softmax_scale, int32_t n_splits,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nomas_segment_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results, without the workspace. The call
+ * allocates nothing; its workspace is a scratch array inside the library,
+ * nomas_segment_attention_noalloc_max_bytes() bytes on every GPU it runs on,
+ * held until the process ends.
+ * Sizes whose workspace (nomas_segment_attention_workspace_bytes) exceeds that
+ * limit give NOMAS_E_WORKSPACE before anything is enqueued; the limit covers
+ * the full single-layer shape (16 x 128 heads, 7,936 queries) without splits.
+ * `stream` must belong to the calling thread's current device (NOMAS_E_INVALID
+ * otherwise). Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (other streams, other threads) race and must be ordered
+ * by the caller. The first call on a device looks up the array's address there.
+ */
+size_t  nomas_segment_attention_noalloc_max_bytes(void);
+int32_t nomas_segment_attention_noalloc(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                        int64_t ld_qkv, int32_t n_video, int32_t n_text, const nomas_kvcache* c,
+                                        uint16_t* out, int64_t ld_out, float* lse, float softmax_scale,
+                                        int32_t n_splits, void* stream);
 
 /*
  * 3D RoPE angles of a segment's video rows as a table, for the fused projection

@@ -46,6 +46,7 @@
 //    share (head, split): they stream the same K/V through that XCD's L2.
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "nomas_common.hpp"
@@ -1183,6 +1184,67 @@ extern "C" int32_t nomas_segment_attention_sparse(const uint16_t* q, const uint1
                                                   size_t workspace_bytes, void* stream) {
   return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, true, block_list, n_select, out, ld_out,
                                 lse, softmax_scale, n_splits, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// The workspace of nomas_segment_attention_noalloc: a device array of the
+// library, one copy on every GPU it runs on, held until the process ends. Host
+// code never passes the array's name to a kernel or a copy (in host code it is
+// a stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for the current device, looked up on the entry point's first call
+// there and kept per device.
+namespace nomas {
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int32_t scratch_address(void** out, const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NOMAS_E_HIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(NOMAS_E_UNSUPPORTED, "%s: device %d beyond %d", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(NOMAS_E_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", who, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NOMAS_OK;
+}
+}  // namespace nomas
+
+extern "C" size_t nomas_segment_attention_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int32_t nomas_segment_attention_noalloc(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                                   int64_t ld_qkv, int32_t n_video, int32_t n_text,
+                                                   const nomas_kvcache* c, uint16_t* out, int64_t ld_out,
+                                                   float* lse, float softmax_scale, int32_t n_splits, void* stream) {
+  const char* who = "segment_attention_noalloc";
+  if (int32_t e = validate_cache(c, who)) return e;
+  // the workspace these sizes need must fit the scratch array (checked before
+  // anything touches the device)
+  const size_t need = nomas_segment_attention_workspace_bytes(
+      n_video, n_text, nomas_kvcache_valid_frames(c) * c->tokens_per_frame, c->n_heads, c->head_dim, c->kv_dtype,
+      n_splits);
+  if (need == 0) return fail(NOMAS_E_INVALID, "%s: sizes out of range", who);
+  if (need > kNoAllocScratchBytes)
+    return fail(NOMAS_E_WORKSPACE, "%s: these sizes need %zu bytes of workspace, beyond the %zu-byte scratch array",
+                who, need, kNoAllocScratchBytes);
+  if (stream) {
+    int sdev = -1, cur = -1;
+    if (hipStreamGetDevice(as_stream(stream), &sdev) != hipSuccess || hipGetDevice(&cur) != hipSuccess || sdev != cur)
+      return fail(NOMAS_E_INVALID, "%s: the stream must belong to the calling thread's current device", who);
+  }
+  void* ws = nullptr;
+  if (int32_t e = scratch_address(&ws, who)) return e;
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, false, nullptr, 0, out, ld_out, lse,
+                                softmax_scale, n_splits, ws, kNoAllocScratchBytes, stream);
 }
 
 // ---------------------------------------------------------------- multi-segment calls

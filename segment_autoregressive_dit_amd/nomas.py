@@ -89,6 +89,8 @@ def lib():
                                                  vp, sz, vp]),
         "nomas_block_causal_attention": (i32, [vp, vp, vp, i64, seg_p, i32, i32, i32, i32, i32, vp, i64, vp, f32,
                                                vp, sz, vp]),
+        "nomas_segment_attention_noalloc_max_bytes": (sz, []),
+        "nomas_segment_attention_noalloc": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -278,6 +280,38 @@ def nomas_segment_attention_sparse(q, k_cur, v_cur, n_video, n_text, cache, bloc
     (int32 [H, ceil(n_q/256), n_select], ascending lists of 128-row cache blocks)."""
     return _segment_attention(q, k_cur, v_cur, n_video, n_text, cache, block_list, out, lse, softmax_scale, n_splits,
                               workspace, stream)
+
+
+def nomas_segment_attention_noalloc_max_bytes():
+    return lib().nomas_segment_attention_noalloc_max_bytes()
+
+
+def nomas_segment_attention_noalloc(q, k_cur, v_cur, n_video, n_text, cache, out, lse=None, softmax_scale=None,
+                                    n_splits=0, stream=None):
+    """nomas_segment_attention without a workspace (the library's own scratch
+    array, see nomas.h); nothing is allocated here either, so ``out`` is
+    required. Returns ``out``."""
+    d = cache.desc
+    H, D = d.n_heads, d.head_dim
+    n_q = n_video + n_text
+    qp, ld = _rows_view(q, "q", H, D)
+    kp, ldk = _rows_view(k_cur, "k_cur", H, D)
+    vp, ldv = _rows_view(v_cur, "v_cur", H, D)
+    if not (ld == ldk == ldv):
+        raise ValueError("q, k_cur, v_cur must share a row stride")
+    for t, name in ((q, "q"), (k_cur, "k_cur"), (v_cur, "v_cur"), (out, "out")):
+        if t.shape[0] < n_q:
+            raise ValueError(f"{name} holds fewer than n_video + n_text rows")
+    op, ldo = _rows_view(out, "out", H, D)
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() < H * n_q:
+            raise ValueError("lse must be a contiguous float32 tensor of n_heads*n_q elements")
+        lp = ctypes.c_void_p(lse.data_ptr())
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().nomas_segment_attention_noalloc(qp, kp, vp, ld, n_video, n_text, ctypes.byref(d), op, ldo, lp, scale,
+                                                 n_splits, _stream(stream)))
+    return out
 
 
 def nomas_sparse_candidates(n_cached):

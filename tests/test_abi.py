@@ -305,3 +305,20 @@ def test_qkv_projection_rejects_before_launch():
     assert call(tab=ctypes.c_void_p((1 << 24) + 8)) == nomas.NOMAS_E_INVALID
     assert L.nomas_rope3d_table(p, 128, 0, 1, 2, 2, 32, 48, 40, 10000.0, 0, None) == nomas.NOMAS_E_INVALID
     assert L.nomas_rope3d_table(None, 128, 0, 1, 2, 2, 32, 48, 48, 10000.0, 0, None) == nomas.NOMAS_E_INVALID
+
+
+def test_noalloc_limit_and_refusal_on_the_host():
+    """The no-allocation attention call states its scratch size and refuses
+    sizes beyond it before touching the device (placeholder addresses)."""
+    L = nomas.lib()
+    cap = L.nomas_segment_attention_noalloc_max_bytes()
+    assert cap == 64 << 20
+    # the full single-layer shape without splits fits
+    assert L.nomas_segment_attention_workspace_bytes(7680, 256, 17280, 16, 128, 0, 1) <= cap
+    _, d, rc = _desc(dtype=0, heads=16, dim=128, tpf=960, cap=18)
+    assert rc == 0
+    d.frames_written = 18
+    fake = ctypes.c_void_p(1 << 20)
+    rc = L.nomas_segment_attention_noalloc(fake, fake, fake, 2048, 7680, 256, ctypes.byref(d), fake, 2048, None,
+                                           0.088, 8, None)
+    assert rc == nomas.NOMAS_E_WORKSPACE and b"scratch" in L.nomas_last_error()

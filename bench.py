@@ -200,6 +200,37 @@ class ClockSampler:
         return statistics.median(self.samples) if self.samples else None
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def time_launches(fn, reps):
+    """Mean GPU time (ms) of ``reps`` back-to-back launches of ``fn``. A spin
+    kernel holds the GPU for a few ms first, so the host has enqueued the whole
+    batch before it starts: the events then bracket GPU work only, not the
+    host's launch overhead (which exceeds a short kernel's run time)."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * (5 + 0.1 * reps)))
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def layer_int8_bench(reps=20):
     """The single-layer shape with an INT8 window (16x128 heads, 18 frames of
     24x40, 4 outlier key channels per head at 20x): the attention launch and the
@@ -218,20 +249,7 @@ def layer_int8_bench(reps=20):
     ws = nomas.workspace_for(cache, wl.n_video, wl.n_text)
     attn = lambda: nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
     app = lambda: cache.nomas_kvcache_append(k, v, F)
-    res = {}
-    for name, fn in (("attention", attn), ("append", app)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ms = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms.append(e0.elapsed_time(e1))
-        res[name] = statistics.median(ms)
+    res = {"attention": time_launches(attn, reps), "append": time_launches(app, 5 * reps)}
     flop = wl.attention_flop()
     # read K, V bf16 + write K, V codes + one fp32 scale per (token, head) each
     app_bytes = 2 * wl.n_video * H * D * 2 + 2 * wl.n_video * H * D + 2 * wl.n_video * H * 4
@@ -420,18 +438,7 @@ def sparse_layer_bench(reps=20):
     sel = lambda: nomas.nomas_sparse_select(q, wl.n_q, cache, n_sel, block_list=lists, workspace=ws_sel)
     att = lambda: nomas.nomas_segment_attention_sparse(q, k, v, wl.n_video, wl.n_text, cache, lists, out=out,
                                                        workspace=ws)
-    times = {}
-    for name, fn in (("select", sel), ("attention", att)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        times[name] = e0.elapsed_time(e1) / reps
+    times = {"select": time_launches(sel, reps), "attention": time_launches(att, reps)}
     flop = 4 * wl.n_q * (n_sel * 128 + wl.n_q) * D * H
     log(f"[bench] sparse layer: select {times['select'] * 1e3:.1f} us, attention {times['attention']:.3f} ms "
         f"({flop / times['attention'] / 1e9:.1f} TFLOP/s on the kept keys)")
@@ -453,16 +460,7 @@ def qkv_bench(reps=20):
     y = torch.empty((wl.n_q, 3 * H * D), dtype=torch.bfloat16, device="cuda")
     table = nomas.nomas_rope3d_table(D, wl.t0, wl.seg_frames, wl.grid_h, wl.grid_w, wl.rope_split)
     fn = lambda: nomas.nomas_qkv_projection(x, w, H, D, n_video=wl.n_video, rope_table=table, qkv=y)
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms = time_launches(fn, reps)
     flop = 2 * wl.n_q * hidden * 3 * H * D
     log(f"[bench] qkv projection + RoPE: {ms * 1e3:.1f} us, {flop / ms / 1e9:.1f} TFLOP/s")
     return dict(qkv_us=round(ms * 1e3, 2), qkv_tflops=round(flop / ms / 1e9, 1))

@@ -14,18 +14,14 @@
 // An append of n frames writes only its last min(n, capacity) frames, so no two
 // tokens of one launch target the same slot and the launch is race-free.
 //
-// INT8 kernel: one block = 64 tokens of one head. Each token's head_dim values
-// are spread over head_dim/8 consecutive lanes (16-byte chunks), which reduce
-// the absmax with lane shuffles. K rows are written token-major; V is written
-// transposed ([head][dim][token]) through an LDS tile so that each wave stores
-// whole 64-token runs of one dim. The BF16 cache has a copy kernel of its own
-// (kv_append_bf16_kernel, below).
+// INT8 kernel (kv_append_i8_kernel): one block = 128 tokens of one head; codes
+// from a reciprocal product with an exact test that sends the rare codes near a
+// rounding boundary to the IEEE quotient; V transposed in registers. The BF16
+// cache has a copy kernel of its own (kv_append_bf16_kernel). Both are described
+// where they are defined.
 #include "nomas_common.hpp"
 
 namespace nomas {
-
-constexpr int kAppTok = 64;
-constexpr int kAppThreads = 256;
 
 struct AppendArgs {
   const uint16_t* k_new;
@@ -50,93 +46,172 @@ __device__ __forceinline__ int slot_token(const AppendArgs& a, int r) {
   return slot * a.tpf + (r - fi * a.tpf);
 }
 
-// Correctly rounded float32 quotient; the build keeps IEEE division (no fast-math).
-__device__ __forceinline__ float div_rn(float x, float y) { return x / y; }
+// ---- INT8 codes. A vector with absmax m has the scale s = fp32(m / 127) (a
+// correctly rounded division) and x the code RNE(fp32(x / s)). The kernel forms
+// it from the exact product x * r, r = rcp(s) (within 1 ulp of 1/s): with
+// C = 1.5 * 2^23, f = fma(x, r, C) is C + RNE(x * r) (one rounding, to an
+// integer, ties to even), and d = fma(x, r, C - f) is the distance of x * r from
+// that integer. |x*r - x/s| <= 127 * 2^-23 and |fp32(x/s) - x/s| <= 127 * 2^-24,
+// so while |d| <= 1/2 - 2^-14 no half-integer lies between x * r and fp32(x/s)
+// and both round to the same code. Otherwise (about one code in 8,000), and for
+// scales of 0 or below 2^-120 (rcp would overflow, and the scale's own rounding
+// can then push |x/s| past 127.5), the code comes from the IEEE quotient,
+// clamped. A code c is carried as the float C + c, whose low byte is c in two's
+// complement.
+constexpr float kMagic = 12582912.0f;            // 1.5 * 2^23
+constexpr float kNearHalf = 0.5f - 0x1p-14f;
+constexpr float kMinFastScale = 0x1p-120f;
 
-template <int D, bool VEC4>
-__global__ __launch_bounds__(kAppThreads) void kv_append_kernel(AppendArgs a) {
-  constexpr int CPR = D / 8;                       // chunks per token row
-  constexpr int CHUNKS = kAppTok * CPR;
-  constexpr int PER_THREAD = CHUNKS / kAppThreads;
-  constexpr int ROWB = kAppTok + 16;               // padded LDS row of the V^T code tile (bytes)
-  __shared__ __align__(16) unsigned char vt[D * ROWB];
-  __shared__ int slots[kAppTok];
+__device__ __forceinline__ float code_exact(float x, float s) {
+  const bool pos = s > 0.f;
+  const float q = fminf(fmaxf(rintf(x / (pos ? s : 1.f)), -127.f), 127.f);
+  return (pos ? q : 0.f) + kMagic;
+}
 
-  const int h = blockIdx.y;
-  const int tok0 = blockIdx.x * kAppTok;
-  const int tid = threadIdx.x;
-  if (tid < kAppTok) slots[tid] = tok0 + tid < a.rows ? slot_token(a, tok0 + tid) : 0;
-  __syncthreads();
+// low bytes of four code floats -> one dword (bytes in argument order)
+__device__ __forceinline__ unsigned pack4(float c0, float c1, float c2, float c3) {
+  const unsigned lo = __builtin_amdgcn_perm(__float_as_uint(c1), __float_as_uint(c0), 0x0c0c0400u);
+  const unsigned hi = __builtin_amdgcn_perm(__float_as_uint(c3), __float_as_uint(c2), 0x04000c0cu);
+  return lo | hi;
+}
 
+// max |x| over the 8 bf16 of a 16-byte chunk (on the bit patterns: for values
+// >= 0 the order of the patterns is the order of the values), as a float
+__device__ __forceinline__ float absmax8(const u32x4 w) {
+  typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+  // (each element copied to a scalar before its bit cast: a bit cast of a
+  // vector element reads element 0 with this compiler)
+  const unsigned w0 = w[0] & 0x7fff7fffu;
+  u16x2 m = __builtin_bit_cast(u16x2, w0);
 #pragma unroll
-  for (int it = 0; it < PER_THREAD; ++it) {
-    const int c = tid + it * kAppThreads;
-    const int t = c / CPR, cc = c - t * CPR;       // lanes of one token are consecutive
-    const int r = tok0 + t;
-    const bool live = r < a.rows;
-    const int64_t src = (int64_t)r * a.ld + (int64_t)h * D + cc * 8;
-    u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-    if (live) {
-      kx = *reinterpret_cast<const u32x4*>(a.k_new + src);
-      vx = *reinterpret_cast<const u32x4*>(a.v_new + src);
-    }
-    const int st = slots[t];
-    const int64_t krow = ((int64_t)h * a.pitch + st) * D + cc * 8;
-    {
-      float kf[8], vf[8];
-      float km = 0.f, vm = 0.f;
+  for (int e = 1; e < 4; ++e) {
+    const unsigned we = w[e] & 0x7fff7fffu;
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, we));
+  }
+  const unsigned mx = m[0] > m[1] ? m[0] : m[1];
+  return __uint_as_float(mx << 16);
+}
+
+// the 8 codes (as C + code floats) of one token's 16-byte chunk
+__device__ __forceinline__ bool codes8(const u32x4 w, float s, float r, float (&f)[8]) {
+  bool ok = true;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = bf16_lo(kx[e]);
-        kf[2 * e + 1] = bf16_hi(kx[e]);
-        vf[2 * e] = bf16_lo(vx[e]);
-        vf[2 * e + 1] = bf16_hi(vx[e]);
-      }
+  for (int e = 0; e < 8; ++e) {
+    const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    f[e] = fmaf(x, r, kMagic);
+    const float d = fmaf(x, r, kMagic - f[e]);
+    ok &= fabsf(d) <= kNearHalf;          // false for NaN (r of a small scale)
+  }
+  if (!ok) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        km = fmaxf(km, fabsf(kf[e]));
-        vm = fmaxf(vm, fabsf(vf[e]));
-      }
+    for (int e = 0; e < 8; ++e) f[e] = code_exact((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]), s);
+  }
+  return ok;
+}
+
+// One block = 128 tokens x D channels of one head, D/32 waves; wave w owns
+// channels [32w, 32w+32). Lane = tg + 16*cc: tokens 8tg..8tg+7 of the block,
+// channels 32w + 8cc .. +8, so a lane loads 8 rows x 16 bytes of K and of V.
+// A token's absmax: over the lane's chunk, then over the wave's 4 chunk lanes
+// (two row swaps, which leave the K maxima in rows 0 and 2 and the V maxima in
+// rows 1 and 3), then across waves through LDS; one thread per (token, K or V)
+// then forms the scale and its reciprocal. K codes go out as 8-byte row pieces;
+// V codes are transposed in registers (8 tokens x 8 channels), so 16 lanes
+// store a 128-byte run of one channel's tokens. VEC8 (tokens per frame a
+// multiple of 8): a lane's 8 tokens sit in 8 consecutive slots; otherwise V^T
+// goes out byte by byte.
+template <int D, bool VEC8>
+__global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
+  constexpr int NW = D / 32, NT = 2 * D, TOK = 128;
+  __shared__ __align__(16) float red[NW][2][TOK];    // per-wave absmax of each token (K, V)
+  __shared__ __align__(16) float2 sr[2][TOK];         // (scale, reciprocal) of each token (K, V)
+  const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tg = lane & 15, cc = lane >> 4;
+  const int tok0 = blockIdx.x * TOK;
+  const int r0 = tok0 + 8 * tg;                    // the lane's first row
+  const int c0 = 32 * wave + 8 * cc;               // and first channel
+
+  u32x4 kx[8], vx[8];
 #pragma unroll
-      for (int m = CPR / 2; m >= 1; m >>= 1) {
-        km = fmaxf(km, __shfl_xor(km, m, CPR));
-        vm = fmaxf(vm, __shfl_xor(vm, m, CPR));
-      }
-      const float ksc = div_rn(km, 127.f), vsc = div_rn(vm, 127.f);
-      unsigned kq[2] = {0, 0}, vq[2] = {0, 0};
+  for (int i = 0; i < 8; ++i) {   // rows past the end re-read the last row and are not stored
+    const int64_t src = (int64_t)min(r0 + i, a.rows - 1) * a.ld + (int64_t)h * D + c0;
+    kx[i] = *reinterpret_cast<const u32x4*>(a.k_new + src);
+    vx[i] = *reinterpret_cast<const u32x4*>(a.v_new + src);
+  }
+
+  // ---- absmax of each token
+  float mx[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kr = km > 0.f ? fminf(fmaxf(rintf(div_rn(kf[e], ksc)), -127.f), 127.f) : 0.f;
-        const float vr = vm > 0.f ? fminf(fmaxf(rintf(div_rn(vf[e], vsc)), -127.f), 127.f) : 0.f;
-        kq[e / 4] |= (static_cast<unsigned>(static_cast<int>(kr)) & 0xffu) << (8 * (e % 4));
-        vq[e / 4] |= (static_cast<unsigned>(static_cast<int>(vr)) & 0xffu) << (8 * (e % 4));
-        vt[(cc * 8 + e) * ROWB + t] = static_cast<unsigned char>(static_cast<int>(vr) & 0xff);
-      }
-      if (live) {
-        *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.kc) + krow) = make_uint2(kq[0], kq[1]);
-        if (cc == 0) {
-          a.ks[(int64_t)h * a.pitch + st] = ksc;
-          a.vs[(int64_t)h * a.pitch + st] = vsc;
-        }
-      }
-    }
+  for (int i = 0; i < 8; ++i) {
+    const float mk = absmax8(kx[i]), mv = absmax8(vx[i]);
+    // rows 0, 2 <- max(K of rows 0|1, 2|3); rows 1, 3 <- max(V of rows 0|1, 2|3)
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(mk), __float_as_uint(mv), false, false);
+    const float m2 = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const unsigned u2 = __float_as_uint(m2);
+    const auto q = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+    mx[i] = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  }
+  if (cc < 2) {   // row 0 holds the K maxima, row 1 the V maxima of tokens 8tg..8tg+7
+    *reinterpret_cast<f32x4*>(&red[wave][cc][8 * tg]) = (f32x4){mx[0], mx[1], mx[2], mx[3]};
+    *reinterpret_cast<f32x4*>(&red[wave][cc][8 * tg + 4]) = (f32x4){mx[4], mx[5], mx[6], mx[7]};
   }
   __syncthreads();
+  // ---- scales: one (token, K or V) per thread
+  for (int p = tid; p < 2 * TOK; p += NT) {
+    const int kv = p / TOK, t = p % TOK;
+    float m = red[0][kv][t];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w][kv][t]);
+    const float sc = m / 127.0f;
+    const float rc = sc >= kMinFastScale ? __builtin_amdgcn_rcpf(sc) : __builtin_nanf("");
+    sr[kv][t] = make_float2(sc, rc);
+    if (tok0 + t < a.rows) (kv ? a.vs : a.ks)[(int64_t)h * a.pitch + slot_token(a, tok0 + t)] = sc;
+  }
+  __syncthreads();
+  if (r0 >= a.rows) return;
 
-  // transposed V store: lanes run along tokens (4 per lane), waves along dims
-  const int n_live = min(kAppTok, a.rows - tok0);
-  constexpr int GROUPS = kAppTok / 4;
-  for (int i = tid; i < D * GROUPS; i += kAppThreads) {
-    const int d = i / GROUPS, g = i - d * GROUPS;
-    const int t = 4 * g;
-    if (t >= n_live) continue;
-    const int64_t vrow = ((int64_t)h * D + d) * a.pitch;
-    if (VEC4) {   // 4 tokens of one frame, contiguous and aligned slots
-      *reinterpret_cast<unsigned*>(static_cast<int8_t*>(a.vc) + vrow + slots[t]) =
-          *reinterpret_cast<const unsigned*>(&vt[d * ROWB + t]);
-    } else {
-      for (int e = 0; e < 4 && t + e < n_live; ++e)
-        static_cast<int8_t*>(a.vc)[vrow + slots[t + e]] = static_cast<int8_t>(vt[d * ROWB + t + e]);
+  int slot[8];
+  if constexpr (VEC8) {   // rows is a multiple of tpf, so all 8 rows are live
+    const int s0 = slot_token(a, r0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) slot[i] = s0 + i;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) slot[i] = r0 + i < a.rows ? slot_token(a, r0 + i) : -1;
+  }
+
+  // ---- K: codes token by token, 8-byte row pieces
+  int8_t* kc = static_cast<int8_t*>(a.kc) + (int64_t)h * a.pitch * D + c0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float2 q = sr[0][8 * tg + i];
+    float f[8];
+    codes8(kx[i], q.x, q.y, f);
+    if (VEC8 || slot[i] >= 0)
+      *reinterpret_cast<uint2*>(kc + (int64_t)slot[i] * D) = make_uint2(pack4(f[0], f[1], f[2], f[3]),
+                                                                       pack4(f[4], f[5], f[6], f[7]));
+  }
+
+  // ---- V: codes of 8 tokens x 8 channels, transposed to channel rows
+  float fv[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float2 q = sr[1][8 * tg + i];
+    codes8(vx[i], q.x, q.y, fv[i]);
+  }
+  int8_t* vc = static_cast<int8_t*>(a.vc) + ((int64_t)h * D + c0) * a.pitch;
+  if constexpr (VEC8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint2*>(vc + (int64_t)e * a.pitch + slot[0]) =
+          make_uint2(pack4(fv[0][e], fv[1][e], fv[2][e], fv[3][e]), pack4(fv[4][e], fv[5][e], fv[6][e], fv[7][e]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (slot[i] < 0) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vc[(int64_t)e * a.pitch + slot[i]] = static_cast<int8_t>(__float_as_uint(fv[i][e]) & 0xffu);
     }
   }
 }
@@ -201,12 +276,12 @@ static void launch_append_bf16(const AppendArgs& a, bool vec8, hipStream_t s) {
 }
 
 template <int D>
-static void launch_append_int8(const AppendArgs& a, bool vec4, hipStream_t s) {
-  const dim3 grid((unsigned)((a.rows + kAppTok - 1) / kAppTok), (unsigned)a.n_heads);
-  if (vec4)
-    hipLaunchKernelGGL((kv_append_kernel<D, true>), grid, dim3(kAppThreads), 0, s, a);
+static void launch_append_int8(const AppendArgs& a, bool vec8, hipStream_t s) {
+  const dim3 grid((unsigned)((a.rows + 127) / 128), (unsigned)a.n_heads);
+  if (vec8)
+    hipLaunchKernelGGL((kv_append_i8_kernel<D, true>), grid, dim3(2 * D), 0, s, a);
   else
-    hipLaunchKernelGGL((kv_append_kernel<D, false>), grid, dim3(kAppThreads), 0, s, a);
+    hipLaunchKernelGGL((kv_append_i8_kernel<D, false>), grid, dim3(2 * D), 0, s, a);
 }
 
 int32_t validate_cache(const nomas_kvcache* c, const char* who) {
@@ -257,15 +332,15 @@ extern "C" int32_t nomas_kvcache_append(nomas_kvcache* c, const uint16_t* k_new,
   a.vc = c->v;
   a.ks = c->k_scale;
   a.vs = c->v_scale;
-  const bool vec4 = tpf % 4 == 0;
+  const bool vec8 = tpf % 8 == 0;
   const hipStream_t s = as_stream(stream);
   const bool int8 = c->kv_dtype == NOMAS_KV_INT8;
   if (D == 128) {
-    if (int8) launch_append_int8<128>(a, vec4, s);
-    else launch_append_bf16<128>(a, tpf % 8 == 0, s);
+    if (int8) launch_append_int8<128>(a, vec8, s);
+    else launch_append_bf16<128>(a, vec8, s);
   } else {
-    if (int8) launch_append_int8<64>(a, vec4, s);
-    else launch_append_bf16<64>(a, tpf % 8 == 0, s);
+    if (int8) launch_append_int8<64>(a, vec8, s);
+    else launch_append_bf16<64>(a, vec8, s);
   }
   if (int32_t e = check_launch("kvcache_append")) return e;
   c->frames_written += n_frames;

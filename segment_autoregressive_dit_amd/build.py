@@ -29,13 +29,27 @@ FLAGS = [
 ]
 
 
-def build(verbose=True, jobs=4):
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the library's host
+# code (argument checks, planning, ring arithmetic, archive bookkeeping); the
+# device code is built as usual. Load such a build with the ASan runtime
+# preloaded (ASAN_RUNTIME below).
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_RUNTIME = os.path.join(os.path.dirname(HIPCC), "..", "lib", "llvm", "lib", "clang", "22", "lib", "linux",
+                            "libclang_rt.asan-x86_64.so")
+
+
+def build(verbose=True, jobs=4, sanitize=False, out=None):
+    """Compile every source for gfx950 and link ``out`` (default: libnomas.so
+    next to this file). ``sanitize``: host code with ASan + UBSan."""
+    lib = out or LIB
+    extra = SANITIZE_FLAGS if sanitize else []
     with tempfile.TemporaryDirectory(prefix="nomas_build_") as tmp:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC] + FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
             procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
             objs.append(obj)
         failed = False
@@ -49,15 +63,17 @@ def build(verbose=True, jobs=4):
                 sys.stderr.write(out + "\n")
         if failed:
             raise RuntimeError("libnomas build failed")
-        tmp_lib = LIB + ".tmp"
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs
+        tmp_lib = lib + ".tmp"
+        link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+                      "-shared-libsan"] if sanitize else []
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + link_extra + ["-o", tmp_lib] + objs
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("libnomas link failed:\n" + r.stdout + r.stderr)
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

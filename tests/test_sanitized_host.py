@@ -1,7 +1,7 @@
 """The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
 Builds libnomas with the host side instrumented (address and undefined-behaviour
-no recovery; device code as usual) and runs the C-ABI checks of test_abi.py
+sanitizers, no recovery; device code as usual) and runs the C-ABI checks of test_abi.py
 against it in a child process with the ASan runtime preloaded: every argument
 check, size plan and descriptor update those tests reach runs instrumented, and
 any out-of-bounds access, use after free or undefined behaviour ends the child

@@ -292,6 +292,28 @@ int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t n_rows, in
                              const float* rope_table, uint16_t* qkv, int64_t ld_qkv, void* stream);
 
 /*
+ * nomas_qkv_projection for a segment's final denoising step, fused with
+ * nomas_kvcache_append: besides writing qkv exactly as nomas_qkv_projection
+ * does, it appends the segment's n_video / tokens_per_frame frames to the ring
+ * cache `*c` (host descriptor) from the projection's own outputs -- the key
+ * channels of rows [0, n_video) as stored in qkv (rotated when rope_table is
+ * given) and the value channels -- with the append's arithmetic: INT8 scale
+ * m/127 and codes RNE(x/s) of the stored bf16 values, or bf16 copies; the same
+ * slots, eviction and frames_written update. The cache's separate append pass
+ * (a second read of the segment's keys and values) is not needed.
+ * Pages: the projection as above; the cache and its INT8 window as in
+ * nomas_kvcache_append ("Hy-Nomas auf einer RTX 4090", inferencekey.com,
+ * "Modell und Dateien" and "Das Single-GPU-Preset").
+ * c: n_heads and head_dim those of the projection; n_video a positive multiple
+ * of its tokens_per_frame. Other arguments and errors as nomas_qkv_projection;
+ * on an error nothing is enqueued and *c is unchanged.
+ */
+int32_t nomas_qkv_projection_append(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
+                                    const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
+                                    int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
+                                    nomas_kvcache* c, void* stream);
+
+/*
  * Block-sparse segment attention. After two dense denoising steps the pages keep
  * 25 % of the candidate video blocks ("Hy-Nomas auf einer RTX 4090",
  * inferencekey.com, "Das Single-GPU-Preset", citing the tech report's 6.2); they

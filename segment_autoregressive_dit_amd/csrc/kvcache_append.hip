@@ -46,35 +46,6 @@ __device__ __forceinline__ int slot_token(const AppendArgs& a, int r) {
   return slot * a.tpf + (r - fi * a.tpf);
 }
 
-// ---- INT8 codes. A vector with absmax m has the scale s = fp32(m / 127) (a
-// correctly rounded division) and x the code RNE(fp32(x / s)). The kernel forms
-// it from the exact product x * r, r = rcp(s) (within 1 ulp of 1/s): with
-// C = 1.5 * 2^23, f = fma(x, r, C) is C + RNE(x * r) (one rounding, to an
-// integer, ties to even), and d = fma(x, r, C - f) is the distance of x * r from
-// that integer. |x*r - x/s| <= 127 * 2^-23 and |fp32(x/s) - x/s| <= 127 * 2^-24,
-// so while |d| <= 1/2 - 2^-14 no half-integer lies between x * r and fp32(x/s)
-// and both round to the same code. Otherwise (about one code in 8,000), and for
-// scales of 0 or below 2^-120 (rcp would overflow, and the scale's own rounding
-// can then push |x/s| past 127.5), the code comes from the IEEE quotient,
-// clamped. A code c is carried as the float C + c, whose low byte is c in two's
-// complement.
-constexpr float kMagic = 12582912.0f;            // 1.5 * 2^23
-constexpr float kNearHalf = 0.5f - 0x1p-14f;
-constexpr float kMinFastScale = 0x1p-120f;
-
-__device__ __forceinline__ float code_exact(float x, float s) {
-  const bool pos = s > 0.f;
-  const float q = fminf(fmaxf(rintf(x / (pos ? s : 1.f)), -127.f), 127.f);
-  return (pos ? q : 0.f) + kMagic;
-}
-
-// low bytes of four code floats -> one dword (bytes in argument order)
-__device__ __forceinline__ unsigned pack4(float c0, float c1, float c2, float c3) {
-  const unsigned lo = __builtin_amdgcn_perm(__float_as_uint(c1), __float_as_uint(c0), 0x0c0c0400u);
-  const unsigned hi = __builtin_amdgcn_perm(__float_as_uint(c3), __float_as_uint(c2), 0x04000c0cu);
-  return lo | hi;
-}
-
 // max |x| over the 8 bf16 of a 16-byte chunk (on the bit patterns: for values
 // >= 0 the order of the patterns is the order of the values), as a float
 __device__ __forceinline__ float absmax8(const u32x4 w) {
@@ -92,16 +63,12 @@ __device__ __forceinline__ float absmax8(const u32x4 w) {
   return __uint_as_float(mx << 16);
 }
 
-// the 8 codes (as C + code floats) of one token's 16-byte chunk
+// the 8 codes (as C + code floats, see code_fast / code_exact in
+// nomas_common.hpp) of one token's 16-byte chunk
 __device__ __forceinline__ bool codes8(const u32x4 w, float s, float r, float (&f)[8]) {
   bool ok = true;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-    f[e] = fmaf(x, r, kMagic);
-    const float d = fmaf(x, r, kMagic - f[e]);
-    ok &= fabsf(d) <= kNearHalf;          // false for NaN (r of a small scale)
-  }
+  for (int e = 0; e < 8; ++e) f[e] = code_fast((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]), r, ok);
   if (!ok) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = code_exact((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]), s);
@@ -163,7 +130,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
 #pragma unroll
     for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w][kv][t]);
     const float sc = m / 127.0f;
-    const float rc = sc >= kMinFastScale ? __builtin_amdgcn_rcpf(sc) : __builtin_nanf("");
+    const float rc = code_recip(sc);
     sr[kv][t] = make_float2(sc, rc);
     if (tok0 + t < a.rows) (kv ? a.vs : a.ks)[(int64_t)h * a.pitch + slot_token(a, tok0 + t)] = sc;
   }

@@ -38,4 +38,47 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+
+// ---- INT8 codes (the quantise-append and the fused projection). A vector with
+// absmax m has the scale s = fp32(m / 127) (a correctly rounded division) and x
+// the code RNE(fp32(x / s)). The fast path forms it from the exact product
+// x * r, r = rcp(s) (within 1 ulp of 1/s): with C = 1.5 * 2^23,
+// f = fma(x, r, C) is C + RNE(x * r) (one rounding, to an integer, ties to
+// even), and d = fma(x, r, C - f) is the distance of x * r from that integer.
+// |x*r - x/s| <= 127 * 2^-23 and |fp32(x/s) - x/s| <= 127 * 2^-24, so while
+// |d| <= 1/2 - 2^-14 no half-integer lies between x * r and fp32(x/s) and both
+// round to the same code. Otherwise (about one code in 8,000), and for scales
+// of 0 or below 2^-120 (r is then NaN: rcp would overflow, and the scale's own
+// rounding can push |x/s| past 127.5), the code comes from the IEEE quotient,
+// clamped. A code c is carried as the float C + c, whose low byte is c in two's
+// complement.
+constexpr float kMagic = 12582912.0f;            // 1.5 * 2^23
+constexpr float kNearHalf = 0.5f - 0x1p-14f;
+constexpr float kMinFastScale = 0x1p-120f;
+
+// the reciprocal the fast path multiplies by (NaN sends every code of a scale
+// below 2^-120, or of zero, to the exact path)
+__device__ __forceinline__ float code_recip(float s) {
+  return s >= kMinFastScale ? __builtin_amdgcn_rcpf(s) : __builtin_nanf("");
+}
+// fast code of x (C + code); clears ok when the exact path must decide
+__device__ __forceinline__ float code_fast(float x, float r, bool& ok) {
+  const float f = fmaf(x, r, kMagic);
+  const float d = fmaf(x, r, kMagic - f);
+  ok &= fabsf(d) <= kNearHalf;          // false for NaN
+  return f;
+}
+// exact code of x from the IEEE quotient (C + code)
+__device__ __forceinline__ float code_exact(float x, float s) {
+  const bool pos = s > 0.f;
+  const float q = fminf(fmaxf(rintf(x / (pos ? s : 1.f)), -127.f), 127.f);
+  return (pos ? q : 0.f) + kMagic;
+}
+// low bytes of four code floats -> one dword (bytes in argument order)
+__device__ __forceinline__ unsigned pack4(float c0, float c1, float c2, float c3) {
+  const unsigned lo = __builtin_amdgcn_perm(__float_as_uint(c1), __float_as_uint(c0), 0x0c0c0400u);
+  const unsigned hi = __builtin_amdgcn_perm(__float_as_uint(c3), __float_as_uint(c2), 0x04000c0cu);
+  return lo | hi;
+}
+
 }  // namespace nomas

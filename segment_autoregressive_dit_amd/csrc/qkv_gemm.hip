@@ -73,7 +73,28 @@ struct GemmArgs {
   int tiles_m;          // token tiles
   int n_blocks;
   int per_xcd;
+  // the ring cache written by the final-step variant (video rows
+  // [app_row0, n_video) go to the slots of frames frames_written + skip, ...)
+  void* kc;
+  void* vc;
+  float* ks;
+  float* vs;
+  int pitch;
+  int tpf;
+  int cap;
+  int base_slot;        // slot of the first written frame
+  int app_row0;         // first video row written (rows of frames beyond the capacity are skipped)
 };
+
+// cache token row of video row r (app_row0 <= r < n_video)
+__device__ __forceinline__ int gemm_slot_token(const GemmArgs& a, int r) {
+  const int fi = (r - a.app_row0) / a.tpf;
+  int slot = a.base_slot + fi;
+  if (slot >= a.cap) slot -= a.cap;
+  return slot * a.tpf + r % a.tpf;
+}
+
+enum { kAppNone = 0, kAppBf16 = 1, kAppInt8 = 2 };
 
 // Workgroup barrier without the memory fence __syncthreads() carries (which
 // waits for every outstanding load, the prefetched copies included); the
@@ -85,16 +106,165 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
+// ---- final-step variant: the segment's keys and values (the bf16 values the
+// projection stored) into the ring cache, as the quantise-append would write
+// them. The wave's accumulators hold channels c0 + 16i + 4G .. +3 of tokens
+// t0 + 16j + i16 (G = lane/16, i16 = lane%16); its 64 channels lie in one head
+// of the key or value part (or the query part, which is not cached). INT8: a
+// token's absmax over the head's channels (the lane's 16, the wave's 4 channel
+// lanes by two row swaps, for head dim 128 the partner wave's through LDS),
+// scale m/127, codes by the shared code arithmetic. Keys go out as 4-channel
+// pieces of their cache rows; values are staged in LDS as [channel][token] and
+// leave in 16-token runs of their transposed rows (tokens per frame a multiple
+// of 16; otherwise element by element).
+template <int APP, int TI, int TJ, int WN>
+__device__ __forceinline__ void cache_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][TJ], unsigned char* lds, int c0,
+                                               int t0, int wave, int lane) {
+  constexpr bool I8 = APP == kAppInt8;
+  constexpr int ES = I8 ? 1 : 2;                       // bytes per cached element
+  constexpr int WM = 16 * TI;                          // the wave's channels (64)
+  const int G = lane >> 4, i16 = lane & 15;
+  const int D = a.head_dim;
+  const int part = c0 < a.n_ch ? c0 / a.hd : 3;        // 1: keys, 2: values
+  const int hc = c0 - part * a.hd;                     // channel within the part
+  const int h = hc / D, cin0 = hc % D;                 // head, first channel within the head
+  const bool mine = part == 1 || part == 2;
+  __syncthreads();                                      // every wave is done with the ring
+
+  // INT8 scales: per token j of the lane, s = absmax/127 and its reciprocal
+  float sc[TJ], rc[TJ];
+  if constexpr (I8) {
+    float* red = reinterpret_cast<float*>(lds + GC::S * (GC::WBYTES + GC::XBYTES));   // [NW][WN]
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) m = fmaxf(m, fmaxf(fmaxf(fabsf(acc[i][j][0]), fabsf(acc[i][j][1])),
+                                                     fmaxf(fabsf(acc[i][j][2]), fabsf(acc[i][j][3]))));
+      const unsigned u = __float_as_uint(m);
+      const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      const float m2 = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+      const unsigned u2 = __float_as_uint(m2);
+      const auto q = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+      sc[j] = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+      if (G == 0) red[wave * WN + 16 * j + i16] = sc[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      // head dim 128: the head's other 64 channels are the partner wave's (wave ^ 1)
+      if (D > WM) sc[j] = fmaxf(sc[j], red[(wave ^ 1) * WN + 16 * j + i16]);
+      sc[j] = sc[j] / 127.0f;
+      rc[j] = code_recip(sc[j]);
+    }
+  }
+  if (!mine) return;
+  void* cache = part == 1 ? a.kc : a.vc;
+
+  // scales: by the head's first wave, lanes of channel group 0
+  if constexpr (I8) {
+    if (cin0 == 0 && G == 0) {
+      float* sdst = (part == 1 ? a.ks : a.vs) + (int64_t)h * a.pitch;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int r = t0 + 16 * j + i16;
+        if (r >= a.app_row0 && r < a.n_video) sdst[gemm_slot_token(a, r)] = sc[j];
+      }
+    }
+  }
+
+  // the cached form of element e of acc[i][j]: C + code (INT8) or the bf16 value
+  auto cached = [&](int i, int j, float (&f)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = acc[i][j][e];
+    if constexpr (I8) {
+      bool ok = true;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = code_fast(acc[i][j][e], rc[j], ok);
+      if (!ok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = code_exact(acc[i][j][e], sc[j]);
+      }
+    }
+  };
+
+  if (part == 1) {
+    // keys: 4 channels of one token per store
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int r = t0 + 16 * j + i16;
+      if (r < a.app_row0 || r >= a.n_video) continue;
+      unsigned char* row = static_cast<unsigned char*>(cache) + ((int64_t)h * a.pitch + gemm_slot_token(a, r)) * D * ES;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        float f[4];
+        cached(i, j, f);
+        const int cin = cin0 + 16 * i + 4 * G;
+        if constexpr (I8) *reinterpret_cast<unsigned*>(row + cin) = pack4(f[0], f[1], f[2], f[3]);
+        else *reinterpret_cast<uint2*>(row + 2 * cin) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      }
+    }
+    return;
+  }
+
+  // values: staged [64 channels][WN tokens] in this wave's part of the ring
+  unsigned char* st = lds + wave * WM * WN * ES;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      float f[4];
+      cached(i, j, f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int off = (16 * i + 4 * G + e) * WN + 16 * j + i16;
+        if constexpr (I8) st[off] = static_cast<unsigned char>(__float_as_uint(f[e]) & 0xffu);
+        else reinterpret_cast<uint16_t*>(st)[off] = static_cast<uint16_t>(__float_as_uint(f[e]) >> 16);
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's staging stores have landed
+  unsigned char* vt = static_cast<unsigned char*>(cache) + ((int64_t)h * D + cin0) * a.pitch * ES;
+  if (a.tpf % 16 == 0) {
+    // 8 lanes per channel row, 16 tokens (one run of slots) each
+    constexpr int CH = WN / 16;
+#pragma unroll
+    for (int k = 0; k < WM * CH / 64; ++k) {
+      const int cl = (k * 64 + lane) / CH, chunk = (k * 64 + lane) % CH;
+      const int r = t0 + 16 * chunk;
+      if (r < a.app_row0 || r >= a.n_video) continue;
+      unsigned char* dst = vt + ((int64_t)cl * a.pitch + gemm_slot_token(a, r)) * ES;
+      const unsigned char* src = st + (cl * WN + 16 * chunk) * ES;
+#pragma unroll
+      for (int b = 0; b < ES; ++b)
+        reinterpret_cast<u32x4*>(dst)[b] = reinterpret_cast<const u32x4*>(src)[b];
+    }
+  } else {
+    for (int k = lane; k < WM * WN; k += 64) {
+      const int cl = k / WN, tl = k % WN, r = t0 + tl;
+      if (r < a.app_row0 || r >= a.n_video) continue;
+      unsigned char* dst = vt + ((int64_t)cl * a.pitch + gemm_slot_token(a, r)) * ES;
+      const unsigned char* src = st + (cl * WN + tl) * ES;
+#pragma unroll
+      for (int b = 0; b < ES; ++b) dst[b] = src[b];
+    }
+  }
+}
+
 // s_waitcnt with vmcnt(n), lgkmcnt(0) (expcnt left alone)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
+// APP: kAppNone (the projection alone), kAppBf16 / kAppInt8 (the final-step
+// variant that also writes the segment's keys and values into the ring cache)
+template <int APP>
 __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmArgs a) {
   constexpr int BM = GC::BM, BN = GC::BN, WM = GC::WM, WN = GC::WN, S = GC::S, BK = GC::BK;
   constexpr int TI = GC::TI, TJ = GC::TJ, IPS = GC::IPS;
-  __shared__ __align__(16) unsigned char lds[S * (GC::WBYTES + GC::XBYTES)];
+  // (the final-step variant reuses the ring for its value staging, then 4 KB of
+  // per-wave maxima)
+  __shared__ __align__(16) unsigned char lds[S * (GC::WBYTES + GC::XBYTES) + (APP == kAppInt8 ? GC::NW * WN * 4 : 0)];
   auto wbuf = [&](int st) { return lds + st * (GC::WBYTES + GC::XBYTES); };
   auto xbuf = [&](int st) { return lds + st * (GC::WBYTES + GC::XBYTES) + GC::WBYTES; };
 
@@ -247,9 +417,13 @@ __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmAr
         v[2] = fmaf(u1, cs[i][2], -w1 * cs[i][3]);
         v[3] = fmaf(u1, cs[i][3], w1 * cs[i][2]);
       }
-      *reinterpret_cast<uint2*>(a.y + (int64_t)tok * a.ld_y + ch) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      const unsigned p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(a.y + (int64_t)tok * a.ld_y + ch) = make_uint2(p01, p23);
+      // the final-step variant caches what the projection stored: the bf16 values
+      if constexpr (APP != kAppNone) acc[i][j] = (f32x4){bf16_lo(p01), bf16_hi(p01), bf16_lo(p23), bf16_hi(p23)};
     }
   }
+  if constexpr (APP != kAppNone) cache_epilogue<APP, TI, TJ, WN>(a, acc, lds, ch0 + wch, tok0 + wtok, wave, lane);
 }
 
 // table[i][p] = (cos, sin)(pos_axis(i, p) * w[p]) for the video rows of a segment
@@ -302,11 +476,13 @@ extern "C" int32_t nomas_rope3d_table(float* table, int32_t head_dim, int32_t t0
   return check_launch(who);
 }
 
-extern "C" int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
-                                        const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
-                                        int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
-                                        void* stream) {
-  const char* who = "qkv_projection";
+namespace nomas {
+int32_t validate_cache(const nomas_kvcache* c, const char* who);
+
+static int32_t qkv_projection_impl(const char* who, const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
+                                   const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
+                                   int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
+                                   nomas_kvcache* c, void* stream) {
   if (!x || !w || !qkv) return fail(NOMAS_E_INVALID, "%s: x, w, qkv must be non-NULL", who);
   if (!aligned16(x) || !aligned16(w) || !aligned16(qkv)) return fail(NOMAS_E_INVALID, "%s: x, w, qkv must be 16-byte aligned", who);
   if (rope_table && !aligned16(rope_table)) return fail(NOMAS_E_INVALID, "%s: rope_table must be 16-byte aligned", who);
@@ -319,7 +495,7 @@ extern "C" int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t
     return fail(NOMAS_E_INVALID, "%s: ld_x, ld_w >= hidden (multiples of 8), ld_qkv >= 3*n_heads*head_dim (a multiple of 4)", who);
   if ((int64_t)GC::BM * ld_w * 2 > INT32_MAX || (int64_t)GC::BN * ld_x * 2 > INT32_MAX || n_ch > (1 << 20))
     return fail(NOMAS_E_INVALID, "%s: sizes out of range", who);
-  GemmArgs a;
+  GemmArgs a{};
   a.x = x;
   a.ld_x = ld_x;
   a.n_rows = n_rows;
@@ -337,6 +513,55 @@ extern "C" int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t
   a.tiles_n = (int)((n_ch + GC::BM - 1) / GC::BM);
   a.n_blocks = a.tiles_n * a.tiles_m;
   a.per_xcd = (a.n_blocks + 7) / 8;
-  hipLaunchKernelGGL(qkv_gemm_kernel, dim3((unsigned)(8 * a.per_xcd)), dim3(GC::NT), 0, as_stream(stream), a);
-  return check_launch(who);
+  int app = kAppNone;
+  int n_frames = 0;
+  if (c) {
+    if (int32_t e = validate_cache(c, who)) return e;
+    if (c->n_heads != n_heads || c->head_dim != head_dim)
+      return fail(NOMAS_E_INVALID, "%s: the cache holds %d heads of %d, the projection %d of %d", who, c->n_heads,
+                  c->head_dim, n_heads, head_dim);
+    const int tpf = c->tokens_per_frame, cap = c->capacity_frames;
+    if (n_video < tpf || n_video % tpf)
+      return fail(NOMAS_E_INVALID, "%s: n_video %d must be a positive multiple of tokens_per_frame %d", who, n_video, tpf);
+    n_frames = n_video / tpf;
+    const int skip = n_frames > cap ? n_frames - cap : 0;   // frames overwritten within this append
+    // the cached keys are the stored (rotated) ones; without a table nothing is rotated
+    a.n_video = n_video;
+    a.kc = c->k;
+    a.vc = c->v;
+    a.ks = c->k_scale;
+    a.vs = c->v_scale;
+    a.pitch = c->token_pitch;
+    a.tpf = tpf;
+    a.cap = cap;
+    a.base_slot = (int)((c->frames_written + skip) % cap);
+    a.app_row0 = skip * tpf;
+    app = c->kv_dtype == NOMAS_KV_INT8 ? kAppInt8 : kAppBf16;
+  }
+  const dim3 grid((unsigned)(8 * a.per_xcd)), block(GC::NT);
+  const hipStream_t st = as_stream(stream);
+  if (app == kAppInt8) hipLaunchKernelGGL(qkv_gemm_kernel<kAppInt8>, grid, block, 0, st, a);
+  else if (app == kAppBf16) hipLaunchKernelGGL(qkv_gemm_kernel<kAppBf16>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(qkv_gemm_kernel<kAppNone>, grid, block, 0, st, a);
+  if (int32_t e = check_launch(who)) return e;
+  if (c) c->frames_written += n_frames;
+  return ok();
+}
+}  // namespace nomas
+
+extern "C" int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
+                                        const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
+                                        int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
+                                        void* stream) {
+  return qkv_projection_impl("qkv_projection", x, ld_x, n_rows, hidden, w, ld_w, n_heads, head_dim, n_video,
+                             rope_table, qkv, ld_qkv, nullptr, stream);
+}
+
+extern "C" int32_t nomas_qkv_projection_append(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
+                                               const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
+                                               int32_t n_video, const float* rope_table, uint16_t* qkv,
+                                               int64_t ld_qkv, nomas_kvcache* c, void* stream) {
+  if (!c) return fail(NOMAS_E_INVALID, "qkv_projection_append: cache descriptor is NULL");
+  return qkv_projection_impl("qkv_projection_append", x, ld_x, n_rows, hidden, w, ld_w, n_heads, head_dim, n_video,
+                             rope_table, qkv, ld_qkv, c, stream);
 }

@@ -89,6 +89,7 @@ def lib():
                                                  vp, sz, vp]),
         "nomas_block_causal_attention": (i32, [vp, vp, vp, i64, seg_p, i32, i32, i32, i32, i32, vp, i64, vp, f32,
                                                vp, sz, vp]),
+        "nomas_qkv_projection_append": (i32, [vp, i64, i32, i32, vp, i64, i32, i32, i32, vp, vp, i64, desc_p, vp]),
         "nomas_segment_attention_noalloc_max_bytes": (sz, []),
         "nomas_segment_attention_noalloc": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp]),
     }
@@ -456,9 +457,11 @@ def nomas_rope3d_table(head_dim, t0, n_frames, grid_h, grid_w, band, theta=10000
     return table
 
 
-def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qkv=None, stream=None):
+def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qkv=None, stream=None, cache=None):
     """qkv = [q | k | v] projection of x [n, hidden] by w [3*H*D, hidden] with RoPE
-    on the video rows' q, k (when a table is given). Returns qkv [n, 3*H*D]."""
+    on the video rows' q, k (when a table is given). Returns qkv [n, 3*H*D].
+    With ``cache`` (a KVCache): nomas_qkv_projection_append, which also appends
+    the n_video rows' keys and values to it."""
     for t, name in ((x, "x"), (w, "w")):
         if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
             raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor with unit inner stride")
@@ -476,7 +479,17 @@ def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qk
                 rope_table.numel() < n_video * head_dim:
             raise ValueError("rope_table must be a contiguous float32 tensor of n_video*head_dim elements")
         tp = ctypes.c_void_p(rope_table.data_ptr())
-    _check(lib().nomas_qkv_projection(ctypes.c_void_p(x.data_ptr()), x.stride(0), n, hidden,
-                                      ctypes.c_void_p(w.data_ptr()), w.stride(0), n_heads, head_dim, n_video, tp,
-                                      ctypes.c_void_p(qkv.data_ptr()), qkv.stride(0), _stream(stream)))
+    args = (ctypes.c_void_p(x.data_ptr()), x.stride(0), n, hidden, ctypes.c_void_p(w.data_ptr()), w.stride(0),
+            n_heads, head_dim, n_video, tp, ctypes.c_void_p(qkv.data_ptr()), qkv.stride(0))
+    if cache is None:
+        _check(lib().nomas_qkv_projection(*args, _stream(stream)))
+    else:
+        _check(lib().nomas_qkv_projection_append(*args, ctypes.byref(cache.desc), _stream(stream)))
     return qkv
+
+
+def nomas_qkv_projection_append(x, w, n_heads, head_dim, n_video, rope_table, cache, qkv=None, stream=None):
+    """The final-step projection: nomas_qkv_projection that also appends the
+    n_video rows' keys and values to ``cache``. Returns qkv."""
+    return nomas_qkv_projection(x, w, n_heads, head_dim, n_video=n_video, rope_table=rope_table, qkv=qkv,
+                                stream=stream, cache=cache)

@@ -322,3 +322,16 @@ def test_noalloc_limit_and_refusal_on_the_host():
     rc = L.nomas_segment_attention_noalloc(fake, fake, fake, 2048, 7680, 256, ctypes.byref(d), fake, 2048, None,
                                            0.088, 8, None)
     assert rc == nomas.NOMAS_E_WORKSPACE and b"scratch" in L.nomas_last_error()
+
+
+def test_projection_append_rejects_before_launch_and_keeps_descriptor():
+    L, d, rc = _desc(dtype=1, heads=2, dim=64, tpf=24, cap=4)
+    assert rc == 0
+    p = ctypes.c_void_p(1 << 24)
+    def call(H=2, D=64, nv=48, desc=d):
+        return L.nomas_qkv_projection_append(p, 128, 64, 128, p, 128, H, D, nv, None, p, 384, desc, None)
+    assert call(H=3) == nomas.NOMAS_E_INVALID and b"heads" in L.nomas_last_error()
+    assert call(nv=40) == nomas.NOMAS_E_INVALID and b"multiple" in L.nomas_last_error()
+    assert call(nv=0) == nomas.NOMAS_E_INVALID
+    assert call(desc=None) == nomas.NOMAS_E_INVALID
+    assert d.frames_written == 0

@@ -103,3 +103,84 @@ def test_table_matches_rope_kernel():
     nomas.nomas_rope3d(q, None, 5, F, gh, gw, (32, 48, 48), H, D)
     torch.cuda.synchronize()
     assert torch.equal(y[:, :hidden].reshape(n, H, D), q)
+
+
+def _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed):
+    """Run the final-step projection into a ring cache that already holds
+    ``prior`` frames; return (qkv of the fused call, qkv of the plain call,
+    fused cache, cache filled by the plain projection + nomas_kvcache_append,
+    the ring model of the fused cache with the oracle's quantisation of the
+    stored K/V rows)."""
+    from oracle import quant
+    from oracle.ring import RingModel
+    tpf = gh * gw
+    nv, n = F * tpf, F * tpf + T
+    xb, wb = _data(n, hidden, 3 * H * D, seed)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    t0 = prior
+    table = nomas.nomas_rope3d_table(D, t0, F, gh, gw, (D // 4, 3 * D // 8, 3 * D // 8))
+    caches = [nomas.KVCache(H, D, tpf, cap, int8) for _ in range(2)]
+    for c in caches:   # the same sentinel in both: bytes neither call writes compare equal
+        c.k.fill_(0xA5)
+        c.v.fill_(0xA5)
+        if int8:
+            c.k_scale.fill_(-1.0)
+            c.v_scale.fill_(-1.0)
+    ring = RingModel(cap)
+    if prior:
+        kp = synth.normal_bf16((prior * tpf, H, D), 99, seed, 0, 3)
+        vp = synth.normal_bf16((prior * tpf, H, D), 99, seed, 0, 4)
+        for c in caches:
+            c.nomas_kvcache_append(dev_bf16(kp), dev_bf16(vp), prior)
+        ring.append([None] * prior)
+    say(f"qkv fused append: H={H} D={D} tpf={tpf} F={F} cap={cap} int8={int8} prior={prior}")
+    y_fused = nomas.nomas_qkv_projection_append(x, w, H, D, nv, table, caches[0])
+    y_plain = nomas.nomas_qkv_projection(x, w, H, D, n_video=nv, rope_table=table)
+    caches[1].nomas_kvcache_append(y_plain[:, H * D:2 * H * D], y_plain[:, 2 * H * D:], F)
+    torch.cuda.synchronize()
+    # the oracle's view of what the fused call appended: its own stored K/V rows
+    kv = host_f64(y_fused[:nv]).reshape(nv, 3, H, D)
+    frames = []
+    for f in range(F):
+        kf, vf = kv[f * tpf:(f + 1) * tpf, 1], kv[f * tpf:(f + 1) * tpf, 2]
+        frames.append((quant.quantise(kf), quant.quantise(vf)) if int8 else (kf, vf))
+    ring.append(frames)
+    return y_fused, y_plain, caches, ring, tpf
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize("case", [
+    # H, D, hidden, grid_h, grid_w, frames, text, capacity, prior frames
+    (2, 64, 128, 4, 6, 2, 9, 4, 3),         # tpf 24 (element-wise value path), wraps
+    (3, 128, 256, 4, 8, 3, 17, 4, 0),       # tpf 32 (16-token runs), empty cache, odd heads
+    (2, 128, 128, 2, 8, 5, 0, 3, 1),        # more frames than the capacity, no text
+    (16, 128, 2048, 24, 40, 8, 256, 18, 18),  # the layer shape: full window, every frame evicts
+], ids=["tpf24", "tpf32_h3", "overflow", "layer"])
+def test_projection_append_equals_projection_then_append(case, int8):
+    """The fused final-step call writes the same qkv as the plain projection (bit
+    for bit) and leaves the cache byte for byte as the plain projection followed
+    by nomas_kvcache_append of its key/value views; the appended frames equal the
+    oracle quantiser's codes and scales of the stored bf16 rows (bit-exact) at the
+    ring model's slots; frames_written as the ring model's."""
+    from _gpu_util import cache_slots
+    H, D, hidden, gh, gw, F, T, cap, prior = case
+    y_fused, y_plain, caches, ring, tpf = _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed=3 + F)
+    assert torch.equal(y_fused, y_plain), "the fused call's qkv differs from the plain projection's"
+    for name in ("k", "v", "k_scale", "v_scale"):
+        a, b = getattr(caches[0], name), getattr(caches[1], name)
+        if a is not None:
+            assert torch.equal(a, b), f"cache {name} differs from projection + append"
+    assert caches[0].frames_written == ring.frames_written == caches[1].frames_written
+    kc, vc, ks, vs = cache_slots(caches[0])
+    for slot, (f, p) in ring.expected_slots().items():
+        if p is None:
+            continue
+        sl = slice(slot * tpf, (slot + 1) * tpf)
+        if int8:
+            (qk, sk), (qv, sv) = p
+            assert np.array_equal(kc[sl], qk) and np.array_equal(vc[sl], qv), f"codes of frame {f}"
+            assert np.array_equal(ks[sl].view(np.uint32), sk.view(np.uint32)), f"K scales of frame {f}"
+            assert np.array_equal(vs[sl].view(np.uint32), sv.view(np.uint32)), f"V scales of frame {f}"
+        else:
+            kf, vf = p
+            assert np.array_equal(synth.bf16_bits_to_f64(kc[sl]), kf) and np.array_equal(synth.bf16_bits_to_f64(vc[sl]), vf)

@@ -56,3 +56,31 @@ def attention_tolerance(got, ref):
 def new_cache(wl, int8=None, capacity=None):
     return nomas.KVCache(wl.n_heads, wl.head_dim, wl.tpf, capacity or wl.capacity_frames,
                          wl.kv_int8 if int8 is None else int8)
+
+
+class Guarded:
+    """A device buffer of ``nbytes`` between two sentinel bands of BAND bytes
+    (256-byte aligned payload). ``check()`` asserts that no byte outside the
+    payload changed -- the call under test wrote only where it owns."""
+    BAND = 4096
+    FILL = 0xA5
+
+    def __init__(self, nbytes):
+        self.nbytes = int(nbytes)
+        self.raw = torch.full((self.nbytes + 2 * self.BAND,), self.FILL, dtype=torch.uint8, device="cuda")
+
+    def view(self, dtype, shape):
+        return self.raw[self.BAND:self.BAND + self.nbytes].view(dtype).view(shape)
+
+    def check(self, what):
+        torch.cuda.synchronize()
+        lo, hi = self.raw[:self.BAND], self.raw[self.BAND + self.nbytes:]
+        assert bool((lo == self.FILL).all()) and bool((hi == self.FILL).all()), f"{what}: bytes outside it changed"
+
+
+def guarded_like(t):
+    """A guarded copy of tensor ``t`` (same dtype, shape and contents)."""
+    g = Guarded(t.numel() * t.element_size())
+    v = g.view(t.dtype, tuple(t.shape))
+    v.copy_(t)
+    return g, v

@@ -15,7 +15,7 @@ from oracle import attention, quant
 from oracle.ring import RingModel
 from segment_autoregressive_dit_amd import nomas, synth
 
-from _gpu_util import dev_bf16, host_f64, say
+from _gpu_util import Guarded, dev_bf16, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -95,10 +95,21 @@ def _run(wl, n_splits=0, full=False, with_lse=True, n_video=None, n_text=None, c
         v_bits = np.full_like(v_bits, 0x3F80)
     q, k, v = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits)
     n_q = nv + nt
-    lse = torch.empty(H * n_q, dtype=torch.float32, device="cuda") if with_lse else None
+    # out, lse and the workspace sit between sentinel bands, checked after every call
+    g_lse = Guarded(4 * H * n_q) if with_lse else None
+    lse = g_lse.view(torch.float32, (H * n_q,)) if with_lse else None
+    g_ws = Guarded(max(256, nomas.nomas_segment_attention_workspace_bytes(
+        nv, nt, cache.n_cached, H, D, int(wl.kv_int8), n_splits)))
+    ws = g_ws.view(torch.uint8, (g_ws.nbytes,))
     outs = []
     for _ in range(repeat):
-        outs.append(nomas.nomas_segment_attention(q, k, v, nv, nt, cache, lse=lse, n_splits=n_splits))
+        g_out = Guarded(2 * n_q * H * D)
+        outs.append(nomas.nomas_segment_attention(q, k, v, nv, nt, cache, out=g_out.view(torch.bfloat16, (n_q, H, D)),
+                                                  lse=lse, n_splits=n_splits, workspace=ws))
+        g_out.check("attention out")
+    g_ws.check("attention workspace")
+    if g_lse:
+        g_lse.check("attention lse")
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0]), "results differ between identical calls"
@@ -317,3 +328,22 @@ def test_values_of_one_key_range(D, int8):
             vpf = quant.dequantise(*quant.quantise(vpf))
         ref, _ = attention.segment_attention(x[0], x[1], synth.bf16_bits_to_f64(vc), kpf, vpf, 1.0 / math.sqrt(D))
         _check(host_f64(out), ref, f"values of {part} rows [{lo}, {hi}) only")
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_strided_out_leaves_the_gaps(int8):
+    """Full layer shape with out as a strided view (row stride H*D + 64): the
+    64 columns between rows keep their sentinel bytes, and the values equal the
+    contiguous call's bit for bit."""
+    wl = synth.Workload(**{**synth.WORKLOADS["layer_bf16"].__dict__, "kv_int8": int8})
+    H, D, n_q = wl.n_heads, wl.head_dim, wl.n_q
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, int8)
+    _prefill(wl, cache, RingModel(wl.capacity_frames))
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    say(f"attention: strided out, int8={int8}")
+    wide = torch.full((n_q, H * D + 64), -7.0, dtype=torch.bfloat16, device="cuda")
+    ref = nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache)
+    got = nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=wide[:, :H * D])
+    torch.cuda.synchronize()
+    assert bool((wide[:, H * D:] == -7.0).all()), "bytes between output rows changed"
+    assert torch.equal(got.reshape(n_q, H, D), ref)

@@ -13,7 +13,7 @@ import torch
 from oracle import attention
 from segment_autoregressive_dit_amd import nomas, synth
 
-from _gpu_util import dev_bf16, host_f64, say
+from _gpu_util import Guarded, dev_bf16, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -45,9 +45,16 @@ def _run(segments, tpf, window, H, D, seed=0, rows=None):
     say(f"block causal: {len(segments)} segments tpf={tpf} window={window} H={H} D={D}")
     qb, kb, vb, segs = _inputs(segments, tpf, H, D, seed)
     n_rows = qb.shape[0]
-    lse = torch.empty(H * n_rows, dtype=torch.float32, device="cuda")
+    # out, lse and the workspace sit between sentinel bands, checked after the call
+    g_out, g_lse = Guarded(2 * n_rows * H * D), Guarded(4 * H * n_rows)
+    g_ws = Guarded(max(256, nomas.nomas_block_causal_attention_workspace_bytes(segments, tpf, H, D)))
+    lse = g_lse.view(torch.float32, (H * n_rows,))
     out = nomas.nomas_block_causal_attention(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), segments, tpf,
-                                             -1 if window is None else window, H, D, lse=lse)
+                                             -1 if window is None else window, H, D,
+                                             out=g_out.view(torch.bfloat16, (n_rows, H, D)), lse=lse,
+                                             workspace=g_ws.view(torch.uint8, (g_ws.nbytes,)))
+    for g, what in ((g_out, "block-causal out"), (g_lse, "block-causal lse"), (g_ws, "block-causal workspace")):
+        g.check(what)
     torch.cuda.synchronize()
     got, g_lse = host_f64(out), lse.cpu().numpy().reshape(H, n_rows)
     ref, ref_lse = attention.block_causal_full(segs, window_frames=window, rows=rows, return_lse=True)

@@ -15,7 +15,7 @@ import torch
 from oracle import quant, sparse
 from segment_autoregressive_dit_amd import nomas, synth
 
-from _gpu_util import dev_bf16, host_f64, say
+from _gpu_util import Guarded, dev_bf16, guarded_like, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -158,8 +158,27 @@ def test_layer_select_then_attend_sampled_rows():
     nc = nomas.nomas_sparse_candidates(cache.n_cached)
     assert nc == 135
     say("sparse layer: select + attend")
-    lists = nomas.nomas_sparse_select(q, wl.n_q, cache, 34)
-    out = nomas.nomas_segment_attention_sparse(q, k, v, wl.n_video, wl.n_text, cache, lists)
+    # the block lists, the selection's workspace, out, lse and the attention
+    # workspace sit between sentinel bands; the lists must also come back unchanged
+    nqb = (wl.n_q + 255) // 256
+    g_l = Guarded(4 * H * nqb * 34)
+    g_sw = Guarded(max(256, nomas.lib().nomas_sparse_select_workspace_bytes(wl.n_q, cache.n_cached, H, D)))
+    lists = nomas.nomas_sparse_select(q, wl.n_q, cache, 34, block_list=g_l.view(torch.int32, (H, nqb, 34)),
+                                      workspace=g_sw.view(torch.uint8, (g_sw.nbytes,)))
+    g_l.check("selection block_list")
+    g_sw.check("selection workspace")
+    g_lists, lists_in = guarded_like(lists)
+    g_out = Guarded(2 * wl.n_q * H * D)
+    g_lse = Guarded(4 * H * wl.n_q)
+    g_ws = Guarded(max(256, nomas.nomas_segment_attention_workspace_bytes(wl.n_video, wl.n_text, 34 * 128, H, D, 0)))
+    out = nomas.nomas_segment_attention_sparse(q, k, v, wl.n_video, wl.n_text, cache, lists_in,
+                                               out=g_out.view(torch.bfloat16, (wl.n_q, H, D)),
+                                               lse=g_lse.view(torch.float32, (H * wl.n_q,)),
+                                               workspace=g_ws.view(torch.uint8, (g_ws.nbytes,)))
+    for g, what in ((g_lists, "sparse block_list"), (g_out, "sparse out"), (g_lse, "sparse lse"),
+                    (g_ws, "sparse workspace")):
+        g.check(what)
+    assert torch.equal(lists_in, lists), "the attention call changed its block lists"
     torch.cuda.synchronize()
     got, L = host_f64(out), lists.cpu().numpy()
     xq, xk, xv = (synth.bf16_bits_to_f64(t) for t in (qb, kcb, vcb))

@@ -238,6 +238,39 @@ int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_cur, const 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nomas_segment_attention over a chosen range of the retained frames, with the
+ * segment's values optionally given transposed.
+ * Keys/values: the cached tokens of frames [first_frame, first_frame + n_frames)
+ * (absolute frame numbers, as counted by frames_written; all must be retained:
+ * frames_written - valid_frames <= first_frame, first_frame + n_frames <=
+ * frames_written, n_frames >= 0), then all n_q rows of the current segment.
+ * The range may wrap round the ring. Its use: a segment's final denoising step
+ * whose projection has already written the segment into the cache
+ * (nomas_qkv_projection_append) attends to the window before the segment,
+ * [frames_written - n_seg - W, frames_written - n_seg) in a cache of capacity
+ * W + n_seg. With every retained frame the result is bit-identical to
+ * nomas_segment_attention's (the same key order).
+ * v_t: NULL (values from v_cur, as nomas_segment_attention), or (device) bf16
+ * V^T of the current segment [n_heads*head_dim][ld_vt] -- row h*head_dim + d
+ * holds channel d of head h for rows 0 .. n_q-1, as nomas_qkv_projection_vt
+ * writes it; then v_cur is not read (may be NULL), the in-call transpose is
+ * skipped, and ld_vt >= n_q rounded up to a multiple of 128 (the key tiles
+ * read whole blocks of columns; columns >= n_q are never used), a multiple of 8,
+ * head_dim * ld_vt * 2 < 2^31.
+ * Other arguments, results, arithmetic and workspace (sized for n_cached =
+ * n_frames * tokens_per_frame) as nomas_segment_attention. Frames not retained
+ * or a bad v_t: NOMAS_E_INVALID before anything is enqueued.
+ * Pages: the window of past frames ("Das Single-GPU-Preset", inferencekey.com)
+ * and attention to cached context ("Die Schleife", orcarouter.ai).
+ */
+int32_t nomas_segment_attention_frames(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                       int64_t ld_qkv, const uint16_t* v_t, int64_t ld_vt, int32_t n_video,
+                                       int32_t n_text, const nomas_kvcache* c, int64_t first_frame,
+                                       int32_t n_frames, uint16_t* out, int64_t ld_out, float* lse,
+                                       float softmax_scale, int32_t n_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * nomas_segment_attention for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments and results, without the workspace. The call
@@ -292,6 +325,21 @@ int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t n_rows, in
                              const float* rope_table, uint16_t* qkv, int64_t ld_qkv, void* stream);
 
 /*
+ * nomas_qkv_projection that also writes the value channels transposed:
+ * v_t[h*head_dim + d][r] = qkv[r, 2*n_heads*head_dim + h*head_dim + d] for every
+ * row r < n_rows (the same bf16 values), the layout of attention's value
+ * operand: nomas_segment_attention_frames takes it as v_t and skips its
+ * transpose pass over the segment's values.
+ * v_t: (device) bf16 [n_heads*head_dim][ld_vt], 16-byte aligned, ld_vt >= n_rows
+ * and a multiple of 8; columns >= n_rows are not written. Other arguments,
+ * results and errors as nomas_qkv_projection.
+ */
+int32_t nomas_qkv_projection_vt(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden, const uint16_t* w,
+                                int64_t ld_w, int32_t n_heads, int32_t head_dim, int32_t n_video,
+                                const float* rope_table, uint16_t* qkv, int64_t ld_qkv, uint16_t* v_t,
+                                int64_t ld_vt, void* stream);
+
+/*
  * nomas_qkv_projection for a segment's final denoising step, fused with
  * nomas_kvcache_append: besides writing qkv exactly as nomas_qkv_projection
  * does, it appends the segment's n_video / tokens_per_frame frames to the ring
@@ -305,13 +353,17 @@ int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t n_rows, in
  * nomas_kvcache_append ("Hy-Nomas auf einer RTX 4090", inferencekey.com,
  * "Modell und Dateien" and "Das Single-GPU-Preset").
  * c: n_heads and head_dim those of the projection; n_video a positive multiple
- * of its tokens_per_frame. Other arguments and errors as nomas_qkv_projection;
- * on an error nothing is enqueued and *c is unchanged.
+ * of its tokens_per_frame. v_t, ld_vt: NULL, or the V^T output of
+ * nomas_qkv_projection_vt. Other arguments and errors as nomas_qkv_projection;
+ * on an error nothing is enqueued and *c is unchanged. The final step's
+ * attention then reads the frames before the segment
+ * (nomas_segment_attention_frames), so the cache needs room for the window
+ * plus the segment.
  */
 int32_t nomas_qkv_projection_append(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
                                     const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
                                     int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
-                                    nomas_kvcache* c, void* stream);
+                                    uint16_t* v_t, int64_t ld_vt, nomas_kvcache* c, void* stream);
 
 /*
  * Block-sparse segment attention. After two dense denoising steps the pages keep

@@ -44,6 +44,7 @@
 //    normalised fp32 partial and its log-sum-exp, merged in fixed order.
 //  * Block ids are remapped so the blocks that the hardware places on one XCD
 //    share (head, split): they stream the same K/V through that XCD's L2.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <mutex>
@@ -76,7 +77,10 @@ struct AttnArgs {
   const float* ks;
   const float* vs;
   int pitch_c;
-  int n_cached;
+  int n_cached;            // cache keys attended: c_na + c_nb
+  int c_a0;                // in physical cache tokens: [c_a0, c_a0 + c_na), then [0, c_nb)
+  int c_na;                // (a frame range that wraps round the ring is two runs)
+  int c_nb;
   int n_cur;
   int n_q;
   int H;
@@ -239,9 +243,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const int split = __builtin_amdgcn_readfirstlane(hs % a.n_splits);
   const int h = __builtin_amdgcn_readfirstlane(hs / a.n_splits);
 
-  // cache tiles of this block: all of them, or (sparse) those of its list; the
-  // last listed block may be shorter than 128 rows
-  int tiles_c_b = a.tiles_c, full_c_b = a.n_cached / BC, tiles_total_b = a.tiles_total;
+  // cache tiles of this block: the full tiles of the run [c_a0, c_a0 + c_na),
+  // those of [0, c_nb), then the partial tail of each run; or (sparse) the tiles
+  // of its list, whose last block may be shorter than 128 rows
+  const int full_a = a.c_na / BC;
+  int full_c_b = full_a + a.c_nb / BC;
+  int tiles_c_b = full_c_b + (a.c_na % BC != 0) + (a.c_nb % BC != 0);
+  int tiles_total_b = tiles_c_b + (a.n_cur + BC - 1) / BC;
   const int32_t* blist = nullptr;
   constexpr int TPB = kSpKeyBlock / BC;     // tiles per candidate block
   if constexpr (SP) {
@@ -297,10 +305,12 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     for (int db = 0; db < D / 16; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- buffer descriptors: the range check returns zeros for rows past the valid
-  // cache tokens / the current segment, so those keys' K needs no branch.
+  // ---- buffer descriptors: the range check returns zeros for rows past the
+  // attended cache tokens / the current segment (rows of a partial tile inside
+  // the range that are not attended are masked like those past it).
+  const int c_end = a.c_a0 + a.c_na;   // one past the last physical cache row read
   const __amdgpu_buffer_rsrc_t rk_c = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<char*>(const_cast<void*>(a.kc)) + (int64_t)h * a.pitch_c * D * ES, (short)0, a.n_cached * D * ES, 0x00020000);
+      static_cast<char*>(const_cast<void*>(a.kc)) + (int64_t)h * a.pitch_c * D * ES, (short)0, c_end * D * ES, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv_c = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<char*>(const_cast<void*>(a.vc)) + (int64_t)h * D * a.pitch_c * ES, (short)0, D * a.pitch_c * ES, 0x00020000);
   const __amdgpu_buffer_rsrc_t rk_n = __builtin_amdgcn_make_buffer_rsrc(
@@ -308,12 +318,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const __amdgpu_buffer_rsrc_t rv_n = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.vtcur) + (int64_t)h * D * a.pitch_cur, (short)0, D * a.pitch_cur * 2, 0x00020000);
 
-  // per-key scales of the valid cache tokens (zeros beyond: those keys' values
-  // dequantise to 0)
+  // per-key scales of the attended cache tokens (zeros past the range)
   const __amdgpu_buffer_rsrc_t rks_c = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.ks) + (int64_t)h * a.pitch_c, (short)0, I8 ? a.n_cached * 4 : 0, 0x00020000);
+      const_cast<float*>(a.ks) + (int64_t)h * a.pitch_c, (short)0, I8 ? c_end * 4 : 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t rvs_c = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.vs) + (int64_t)h * a.pitch_c, (short)0, I8 ? a.n_cached * 4 : 0, 0x00020000);
+      const_cast<float*>(a.vs) + (int64_t)h * a.pitch_c, (short)0, I8 ? c_end * 4 : 0, 0x00020000);
 
   // bf16 tiles are copied global -> LDS by the load unit straight into their
   // swizzled places. INT8 cache tiles: the codes are staged through registers
@@ -329,18 +338,43 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   int kbase = 0, kend = 0;
   // Every run of tiles is of one kind, known at compile time: cache tiles
   // (cache_tag true) or tiles of the current segment / joint sequence.
-  // tile t -> (first key inside its part, valid keys)
-  auto tile_info = [&](int t, auto cache_tag, int& key0, int& nvalid) {
+  // tile t -> (first key inside its part, valid keys); the valid keys are the
+  // tile's rows [klo, klo + nvalid) (klo > 0 only for a partial cache tile
+  // moved back to keep its rows inside the head's token_pitch rows)
+  auto tile_rows = [&](int t, auto cache_tag, int& key0, int& nvalid, int& klo) {
     constexpr bool CACHE = decltype(cache_tag)::value;
+    klo = 0;
     if constexpr (MS) {
       key0 = kbase + t * BC;
       nvalid = min(BC, kend - key0);
       return;
     }
     // (the list entry is the same for the whole block: keep it scalar)
-    if (SP && CACHE) key0 = __builtin_amdgcn_readfirstlane(blist[t / TPB]) * kSpKeyBlock + (t % TPB) * BC;
-    else key0 = __builtin_amdgcn_readfirstlane((CACHE ? t : t - tiles_c_b) * BC);
-    nvalid = min(BC, (CACHE ? a.n_cached : a.n_cur) - key0);
+    if constexpr (SP && CACHE) {
+      key0 = __builtin_amdgcn_readfirstlane(blist[t / TPB]) * kSpKeyBlock + (t % TPB) * BC;
+      nvalid = min(BC, a.n_cached - key0);
+    } else if constexpr (CACHE) {
+      // full tiles of the first run, of the second, then the partial tails
+      int k0, n;
+      if (t < full_a) k0 = a.c_a0 + t * BC, n = BC;
+      else if (t < full_c_b) k0 = (t - full_a) * BC, n = BC;
+      else if (t == full_c_b && a.c_na % BC) k0 = a.c_a0 + full_a * BC, n = a.c_na % BC;
+      else k0 = a.c_nb / BC * BC, n = a.c_nb % BC;
+      // a tile reads rows [k0, k0 + BC); the first run's tail can end near the
+      // head's last row, so the read is moved back to end at token_pitch (a
+      // multiple of 128, >= BC) and its leading rows are masked too
+      if (k0 + BC > a.pitch_c) klo = k0 - (a.pitch_c - BC), k0 = a.pitch_c - BC;
+      key0 = __builtin_amdgcn_readfirstlane(k0);
+      nvalid = __builtin_amdgcn_readfirstlane(n);
+      klo = __builtin_amdgcn_readfirstlane(klo);
+    } else {
+      key0 = __builtin_amdgcn_readfirstlane((t - tiles_c_b) * BC);
+      nvalid = min(BC, a.n_cur - key0);
+    }
+  };
+  auto tile_info = [&](int t, auto cache_tag, int& key0, int& nvalid) {
+    int klo;
+    tile_rows(t, cache_tag, key0, nvalid, klo);
   };
 
   // ---- issue the loads of tile t's keys / values into K / V buffer i
@@ -488,12 +522,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   };
   auto wait_copies = [&]() { __builtin_amdgcn_s_waitcnt(0); };
 
-  // zero the values of keys past the end of a partial tile (all waves' data landed)
-  auto zero_tail = [&](int i, int nvalid) {
+  // zero the values of the keys of a partial tile outside its rows [klo, khi)
+  // (all waves' data landed)
+  auto zero_tail = [&](int i, int klo, int khi) {
     unsigned char* Vs = vbuf(i);
     for (int idx = tid; idx < D * BC; idx += C::NT) {
       const int d = idx / BC, k = idx % BC;
-      if (k >= nvalid)
+      if (k < klo || k >= khi)
         *reinterpret_cast<uint16_t*>(Vs + d * BC * 2 + (((k >> 3) ^ swz_v<BC>(d)) * 16) + (k & 7) * 2) = 0;
     }
   };
@@ -560,13 +595,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     logits_from(i, k0, s, scaled_tag);
   };
 
-  // keys past the end of a partial tile never win
-  auto mask_tail = [&](f32x4 (&s)[QB][NKB], int nvalid) {
+  // keys of a partial tile outside its rows [klo, khi) never win
+  auto mask_tail = [&](f32x4 (&s)[QB][NKB], int klo, int khi) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + r >= nvalid) {
+        if (const int key = 32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + r; key < klo || key >= khi) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
           kcs[kb][r] = a.c2;   // a zero scale would turn -inf into NaN
@@ -812,19 +847,19 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   // ---- one partial tile (keys past nvalid masked), unpipelined
   auto run_partial = [&](int t, auto ct) {
     const std::bool_constant<I8 && decltype(ct)::value> scaled_tag;
-    int key0, nvalid;
-    tile_info(t, ct, key0, nvalid);
+    int key0, nvalid, klo;
+    tile_rows(t, ct, key0, nvalid, klo);
     start_k(t, 0, ct);
     start_v(t, 0, ct);
     wait_copies();
     finish_k(t, 0, ct);
     finish_v(t, 0, ct);
     __syncthreads();
-    zero_tail(0, nvalid);
+    zero_tail(0, klo, klo + nvalid);
     __syncthreads();
     f32x4 s[QB][NKB];
     logits(0, s, scaled_tag);
-    mask_tail(s, nvalid);
+    mask_tail(s, klo, klo + nvalid);
     bf16x8 pf[QB][BC / 32];
     probs(s, pf, scaled_tag);
     values(0, pf, no_reads);
@@ -852,13 +887,15 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     }
   } else {
     // this split's tiles: full cache tiles, full current tiles, then the partial
-    // tail of each part (key order does not matter to attention)
+    // tails (one per cache run, one of the segment; key order does not matter
+    // to attention)
     const int full_c = full_c_b, full_n = a.n_cur / BC;
     const int c_lo = min(t_begin, full_c), c_hi = min(t_end, full_c);
     const int n_lo = max(t_begin, tiles_c_b), n_hi = min(t_end, tiles_c_b + full_n);
     run_full(c_lo, c_hi - c_lo, T_{});
     run_full(n_lo, max(0, n_hi - n_lo), F_{});
     if (full_c < tiles_c_b && t_begin <= full_c && full_c < t_end) run_partial(full_c, T_{});
+    if (full_c + 1 < tiles_c_b && t_begin <= full_c + 1 && full_c + 1 < t_end) run_partial(full_c + 1, T_{});
     const int pn = tiles_c_b + full_n;
     if (pn < tiles_total_b && t_begin <= pn && pn < t_end) run_partial(pn, F_{});
   }
@@ -1056,17 +1093,37 @@ extern "C" int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_tex
   return p.splits;
 }
 
-// the cached call, dense (sparse = false) or restricted to the block lists
+// The cached tokens a call attends to, as runs of physical cache tokens:
+// [a0, a0 + na) then [0, nb). All retained frames are read in slot order (one
+// run); a frame range that wraps round the ring is two.
+struct CacheRuns {
+  int64_t a0, na, nb;
+};
+static CacheRuns all_retained(const nomas_kvcache* c) {
+  return CacheRuns{0, nomas_kvcache_valid_frames(c) * c->tokens_per_frame, 0};
+}
+
+// the cached call, dense (sparse = false) or restricted to the block lists; the
+// current values from v_cur (transposed into the workspace) or, when v_t is
+// given, from the caller's V^T [H*D][ld_vt]
 static int32_t segment_attention_impl(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur, int64_t ld_qkv,
-                                      int32_t n_video, int32_t n_text, const nomas_kvcache* c, bool sparse,
+                                      const uint16_t* v_t, int64_t ld_vt, int32_t n_video, int32_t n_text,
+                                      const nomas_kvcache* c, const CacheRuns& runs, bool sparse,
                                       const int32_t* block_list, int32_t n_select, uint16_t* out, int64_t ld_out,
                                       float* lse, float softmax_scale, int32_t n_splits, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   if (int32_t e = validate_cache(c, "segment_attention")) return e;
   const int H = c->n_heads, D = c->head_dim;
-  if (!q || !k_cur || !v_cur || !out) return fail(NOMAS_E_INVALID, "segment_attention: q, k_cur, v_cur, out must be non-NULL");
-  if (!aligned16(q) || !aligned16(k_cur) || !aligned16(v_cur) || !aligned16(out))
+  if (!q || !k_cur || !(v_cur || v_t) || !out)
+    return fail(NOMAS_E_INVALID, "segment_attention: q, k_cur, out and v_cur (or v_t) must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cur) || (v_cur && !aligned16(v_cur)) || !aligned16(out))
     return fail(NOMAS_E_INVALID, "segment_attention: q, k_cur, v_cur, out must be 16-byte aligned");
+  // (key tiles read whole 128-row blocks of V^T columns: ld_vt covers them)
+  if (v_t && (!aligned16(v_t) || ld_vt < round_up((int64_t)n_video + n_text, 128) || ld_vt % 8 ||
+              (int64_t)D * ld_vt * 2 > INT32_MAX))
+    return fail(NOMAS_E_INVALID,
+                "segment_attention: v_t must be 16-byte aligned with ld_vt >= n_video + n_text rounded up to a "
+                "multiple of 128, a multiple of 8, and head_dim * ld_vt * 2 bytes below 2 GiB");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3)) return fail(NOMAS_E_INVALID, "segment_attention: lse must be 4-byte aligned");
   if (ld_qkv < (int64_t)H * D || ld_qkv % 8 || ld_out < (int64_t)H * D || ld_out % 8)
     return fail(NOMAS_E_INVALID, "segment_attention: ld_qkv and ld_out must be >= n_heads*head_dim and multiples of 8");
@@ -1079,7 +1136,7 @@ static int32_t segment_attention_impl(const uint16_t* q, const uint16_t* k_cur, 
   if (((int64_t)n_video + n_text) * ld_qkv * 2 > INT32_MAX ||
       (int64_t)D * round_up((int64_t)n_video + n_text, kTokenAlign) * 2 > INT32_MAX)
     return fail(NOMAS_E_INVALID, "segment_attention: (n_video + n_text) * ld_qkv * 2 bytes must stay below 2 GiB");
-  const int64_t n_cached = nomas_kvcache_valid_frames(c) * c->tokens_per_frame;
+  const int64_t n_cached = runs.na + runs.nb;
   const int64_t n_cand = (n_cached + kSpKeyBlock - 1) / kSpKeyBlock;
   if (sparse) {
     if (n_select < 0 || n_select > n_cand)
@@ -1099,26 +1156,33 @@ static int32_t segment_attention_impl(const uint16_t* q, const uint16_t* k_cur, 
 
   const hipStream_t st = as_stream(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(ws);
-  {
+  const uint16_t* vt = v_t;
+  int pitch_cur = (int)ld_vt;
+  if (!v_t) {
+    uint16_t* vw = reinterpret_cast<uint16_t*>(ws);
     const dim3 grid((unsigned)(p.pitch_cur / 128), (unsigned)H);
-    if (D == 128) hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, v_cur, ld_qkv, p.n_q, vt, p.pitch_cur);
-    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(128), 0, st, v_cur, ld_qkv, p.n_q, vt, p.pitch_cur);
+    if (D == 128) hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, st, v_cur, ld_qkv, p.n_q, vw, p.pitch_cur);
+    else hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(128), 0, st, v_cur, ld_qkv, p.n_q, vw, p.pitch_cur);
     if (int32_t e = check_launch("segment_attention (v transpose)")) return e;
+    vt = vw;
+    pitch_cur = p.pitch_cur;
   }
 
-  AttnArgs a;
+  AttnArgs a{};
   a.q = q;
   a.kcur = k_cur;
   a.ld_qkv = ld_qkv;
   a.vtcur = vt;
-  a.pitch_cur = p.pitch_cur;
+  a.pitch_cur = pitch_cur;
   a.kc = c->k;
   a.vc = c->v;
   a.ks = c->k_scale;
   a.vs = c->v_scale;
   a.pitch_c = c->token_pitch;
   a.n_cached = (int)n_cached;
+  a.c_a0 = (int)runs.a0;
+  a.c_na = (int)runs.na;
+  a.c_nb = (int)runs.nb;
   a.n_cur = p.n_q;
   a.n_q = p.n_q;
   a.H = H;
@@ -1172,8 +1236,33 @@ extern "C" int32_t nomas_segment_attention(const uint16_t* q, const uint16_t* k_
                                            int64_t ld_qkv, int32_t n_video, int32_t n_text, const nomas_kvcache* c,
                                            uint16_t* out, int64_t ld_out, float* lse, float softmax_scale,
                                            int32_t n_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, false, nullptr, 0, out, ld_out, lse,
-                                softmax_scale, n_splits, workspace, workspace_bytes, stream);
+  if (int32_t e = validate_cache(c, "segment_attention")) return e;
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, nullptr, 0, n_video, n_text, c, all_retained(c), false,
+                                nullptr, 0, out, ld_out, lse, softmax_scale, n_splits, workspace, workspace_bytes,
+                                stream);
+}
+
+extern "C" int32_t nomas_segment_attention_frames(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                                  int64_t ld_qkv, const uint16_t* v_t, int64_t ld_vt,
+                                                  int32_t n_video, int32_t n_text, const nomas_kvcache* c,
+                                                  int64_t first_frame, int32_t n_frames, uint16_t* out,
+                                                  int64_t ld_out, float* lse, float softmax_scale, int32_t n_splits,
+                                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "segment_attention_frames";
+  if (int32_t e = validate_cache(c, who)) return e;
+  const int64_t fw = c->frames_written, valid = nomas_kvcache_valid_frames(c);
+  if (n_frames < 0 || first_frame < fw - valid || first_frame + n_frames > fw)
+    return fail(NOMAS_E_INVALID, "%s: frames [%lld, %lld) are not all retained (retained: [%lld, %lld))", who,
+                (long long)first_frame, (long long)first_frame + n_frames, (long long)(fw - valid), (long long)fw);
+  const int64_t tpf = c->tokens_per_frame, cap = c->capacity_frames;
+  CacheRuns runs = all_retained(c);
+  if (n_frames < valid) {
+    const int64_t s = first_frame % cap;
+    const int64_t na = std::min<int64_t>(n_frames, cap - s);
+    runs = CacheRuns{s * tpf, na * tpf, (n_frames - na) * tpf};
+  }
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, v_t, ld_vt, n_video, n_text, c, runs, false, nullptr, 0, out,
+                                ld_out, lse, softmax_scale, n_splits, workspace, workspace_bytes, stream);
 }
 
 extern "C" int32_t nomas_segment_attention_sparse(const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
@@ -1182,8 +1271,10 @@ extern "C" int32_t nomas_segment_attention_sparse(const uint16_t* q, const uint1
                                                   int32_t n_select, uint16_t* out, int64_t ld_out, float* lse,
                                                   float softmax_scale, int32_t n_splits, void* workspace,
                                                   size_t workspace_bytes, void* stream) {
-  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, true, block_list, n_select, out, ld_out,
-                                lse, softmax_scale, n_splits, workspace, workspace_bytes, stream);
+  if (int32_t e = validate_cache(c, "segment_attention_sparse")) return e;
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, nullptr, 0, n_video, n_text, c, all_retained(c), true,
+                                block_list, n_select, out, ld_out, lse, softmax_scale, n_splits, workspace,
+                                workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- no-allocation variant
@@ -1243,8 +1334,9 @@ extern "C" int32_t nomas_segment_attention_noalloc(const uint16_t* q, const uint
   }
   void* ws = nullptr;
   if (int32_t e = scratch_address(&ws, who)) return e;
-  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, n_video, n_text, c, false, nullptr, 0, out, ld_out, lse,
-                                softmax_scale, n_splits, ws, kNoAllocScratchBytes, stream);
+  return segment_attention_impl(q, k_cur, v_cur, ld_qkv, nullptr, 0, n_video, n_text, c, all_retained(c), false,
+                                nullptr, 0, out, ld_out, lse, softmax_scale, n_splits, ws, kNoAllocScratchBytes,
+                                stream);
 }
 
 // ---------------------------------------------------------------- multi-segment calls

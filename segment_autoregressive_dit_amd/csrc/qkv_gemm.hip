@@ -84,6 +84,8 @@ struct GemmArgs {
   int cap;
   int base_slot;        // slot of the first written frame
   int app_row0;         // first video row written (rows of frames beyond the capacity are skipped)
+  uint16_t* vt;         // V^T [H*D][ld_vt] of all rows, or null
+  int64_t ld_vt;
 };
 
 // cache token row of video row r (app_row0 <= r < n_video)
@@ -106,29 +108,33 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
-// ---- final-step variant: the segment's keys and values (the bf16 values the
-// projection stored) into the ring cache, as the quantise-append would write
-// them. The wave's accumulators hold channels c0 + 16i + 4G .. +3 of tokens
-// t0 + 16j + i16 (G = lane/16, i16 = lane%16); its 64 channels lie in one head
-// of the key or value part (or the query part, which is not cached). INT8: a
-// token's absmax over the head's channels (the lane's 16, the wave's 4 channel
-// lanes by two row swaps, for head dim 128 the partner wave's through LDS),
-// scale m/127, codes by the shared code arithmetic. Keys go out as 4-channel
-// pieces of their cache rows; values are staged in LDS as [channel][token] and
-// leave in 16-token runs of their transposed rows (tokens per frame a multiple
-// of 16; otherwise element by element).
-template <int APP, int TI, int TJ, int WN>
-__device__ __forceinline__ void cache_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][TJ], unsigned char* lds, int c0,
-                                               int t0, int wave, int lane) {
+// ---- value and cache epilogue. The wave's accumulators hold channels
+// c0 + 16i + 4G .. +3 of tokens t0 + 16j + i16 (G = lane/16, i16 = lane%16),
+// already the bf16 values the projection stored; its 64 channels lie in one
+// head of the query, key or value part.
+//  * VT: the value channels also go out transposed, V^T[h*D + d][token], for
+//    attention's value operand (which then needs no transpose pass).
+//  * APP (final step): the segment's keys and values into the ring cache as
+//    the quantise-append would write them. INT8: a token's absmax over the head
+//    (the lane's 16 channels, the wave's 4 channel lanes by two row swaps, for
+//    head dim 128 the partner wave's through LDS), scale m/127, codes by the
+//    shared code arithmetic. Keys go out as 4-channel pieces of their cache
+//    rows.
+// Transposed values are staged in LDS as [channel][token] and leave in runs of
+// 16 tokens (cache: tokens per frame a multiple of 16, else element by
+// element).
+template <int APP, bool VT, int TI, int TJ, int WN>
+__device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][TJ], unsigned char* lds, int c0,
+                                            int t0, int wave, int lane) {
   constexpr bool I8 = APP == kAppInt8;
   constexpr int ES = I8 ? 1 : 2;                       // bytes per cached element
   constexpr int WM = 16 * TI;                          // the wave's channels (64)
+  constexpr int CH = WN / 16;                          // 16-token runs per channel row
   const int G = lane >> 4, i16 = lane & 15;
   const int D = a.head_dim;
   const int part = c0 < a.n_ch ? c0 / a.hd : 3;        // 1: keys, 2: values
   const int hc = c0 - part * a.hd;                     // channel within the part
   const int h = hc / D, cin0 = hc % D;                 // head, first channel within the head
-  const bool mine = part == 1 || part == 2;
   __syncthreads();                                      // every wave is done with the ring
 
   // INT8 scales: per token j of the lane, s = absmax/127 and its reciprocal
@@ -158,7 +164,37 @@ __device__ __forceinline__ void cache_epilogue(const GemmArgs& a, f32x4 (&acc)[T
       rc[j] = code_recip(sc[j]);
     }
   }
-  if (!mine) return;
+  unsigned char* st = lds + wave * WM * WN * 2;         // the wave's staging area
+
+  // ---- V^T of every row of the call
+  if (VT && part == 2) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          reinterpret_cast<uint16_t*>(st)[(16 * i + 4 * G + e) * WN + 16 * j + i16] =
+              static_cast<uint16_t>(__float_as_uint(acc[i][j][e]) >> 16);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's staging stores have landed
+    uint16_t* vt = a.vt + (int64_t)hc * a.ld_vt;
+#pragma unroll
+    for (int k = 0; k < WM * CH / 64; ++k) {
+      const int cl = (k * 64 + lane) / CH, chunk = (k * 64 + lane) % CH;
+      const int r = t0 + 16 * chunk;
+      uint16_t* dst = vt + (int64_t)cl * a.ld_vt + r;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(st) + cl * WN + 16 * chunk;
+      if (r + 16 <= a.n_rows) {
+        reinterpret_cast<u32x4*>(dst)[0] = reinterpret_cast<const u32x4*>(src)[0];
+        reinterpret_cast<u32x4*>(dst)[1] = reinterpret_cast<const u32x4*>(src)[1];
+      } else {
+        for (int e = 0; e < 16 && r + e < a.n_rows; ++e) dst[e] = src[e];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // its reads are done before the area is staged again
+  }
+  if constexpr (APP == kAppNone) return;
+  if (part != 1 && part != 2) return;
   void* cache = part == 1 ? a.kc : a.vc;
 
   // scales: by the head's first wave, lanes of channel group 0
@@ -207,8 +243,7 @@ __device__ __forceinline__ void cache_epilogue(const GemmArgs& a, f32x4 (&acc)[T
     return;
   }
 
-  // values: staged [64 channels][WN tokens] in this wave's part of the ring
-  unsigned char* st = lds + wave * WM * WN * ES;
+  // values: staged [64 channels][WN tokens] in the wave's area
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -226,7 +261,6 @@ __device__ __forceinline__ void cache_epilogue(const GemmArgs& a, f32x4 (&acc)[T
   unsigned char* vt = static_cast<unsigned char*>(cache) + ((int64_t)h * D + cin0) * a.pitch * ES;
   if (a.tpf % 16 == 0) {
     // 8 lanes per channel row, 16 tokens (one run of slots) each
-    constexpr int CH = WN / 16;
 #pragma unroll
     for (int k = 0; k < WM * CH / 64; ++k) {
       const int cl = (k * 64 + lane) / CH, chunk = (k * 64 + lane) % CH;
@@ -257,8 +291,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // APP: kAppNone (the projection alone), kAppBf16 / kAppInt8 (the final-step
-// variant that also writes the segment's keys and values into the ring cache)
-template <int APP>
+// variant that also writes the segment's keys and values into the ring cache);
+// VT: the values also go out transposed
+template <int APP, bool VT>
 __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmArgs a) {
   constexpr int BM = GC::BM, BN = GC::BN, WM = GC::WM, WN = GC::WN, S = GC::S, BK = GC::BK;
   constexpr int TI = GC::TI, TJ = GC::TJ, IPS = GC::IPS;
@@ -419,11 +454,11 @@ __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmAr
       }
       const unsigned p01 = pack_bf16x2(v[0], v[1]), p23 = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(a.y + (int64_t)tok * a.ld_y + ch) = make_uint2(p01, p23);
-      // the final-step variant caches what the projection stored: the bf16 values
-      if constexpr (APP != kAppNone) acc[i][j] = (f32x4){bf16_lo(p01), bf16_hi(p01), bf16_lo(p23), bf16_hi(p23)};
+      // the value and cache outputs take what the projection stored: the bf16 values
+      if constexpr (APP != kAppNone || VT) acc[i][j] = (f32x4){bf16_lo(p01), bf16_hi(p01), bf16_lo(p23), bf16_hi(p23)};
     }
   }
-  if constexpr (APP != kAppNone) cache_epilogue<APP, TI, TJ, WN>(a, acc, lds, ch0 + wch, tok0 + wtok, wave, lane);
+  if constexpr (APP != kAppNone || VT) kv_epilogue<APP, VT, TI, TJ, WN>(a, acc, lds, ch0 + wch, tok0 + wtok, wave, lane);
 }
 
 // table[i][p] = (cos, sin)(pos_axis(i, p) * w[p]) for the video rows of a segment
@@ -482,7 +517,7 @@ int32_t validate_cache(const nomas_kvcache* c, const char* who);
 static int32_t qkv_projection_impl(const char* who, const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
                                    const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
                                    int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
-                                   nomas_kvcache* c, void* stream) {
+                                   uint16_t* v_t, int64_t ld_vt, nomas_kvcache* c, void* stream) {
   if (!x || !w || !qkv) return fail(NOMAS_E_INVALID, "%s: x, w, qkv must be non-NULL", who);
   if (!aligned16(x) || !aligned16(w) || !aligned16(qkv)) return fail(NOMAS_E_INVALID, "%s: x, w, qkv must be 16-byte aligned", who);
   if (rope_table && !aligned16(rope_table)) return fail(NOMAS_E_INVALID, "%s: rope_table must be 16-byte aligned", who);
@@ -495,6 +530,8 @@ static int32_t qkv_projection_impl(const char* who, const uint16_t* x, int64_t l
     return fail(NOMAS_E_INVALID, "%s: ld_x, ld_w >= hidden (multiples of 8), ld_qkv >= 3*n_heads*head_dim (a multiple of 4)", who);
   if ((int64_t)GC::BM * ld_w * 2 > INT32_MAX || (int64_t)GC::BN * ld_x * 2 > INT32_MAX || n_ch > (1 << 20))
     return fail(NOMAS_E_INVALID, "%s: sizes out of range", who);
+  if (v_t && (!aligned16(v_t) || ld_vt < n_rows || ld_vt % 8))
+    return fail(NOMAS_E_INVALID, "%s: v_t must be 16-byte aligned with ld_vt >= n_rows and a multiple of 8", who);
   GemmArgs a{};
   a.x = x;
   a.ld_x = ld_x;
@@ -509,6 +546,8 @@ static int32_t qkv_projection_impl(const char* who, const uint16_t* x, int64_t l
   a.table = reinterpret_cast<const float2*>(rope_table);
   a.y = qkv;
   a.ld_y = ld_qkv;
+  a.vt = v_t;
+  a.ld_vt = ld_vt;
   a.tiles_m = (n_rows + GC::BN - 1) / GC::BN;
   a.tiles_n = (int)((n_ch + GC::BM - 1) / GC::BM);
   a.n_blocks = a.tiles_n * a.tiles_m;
@@ -540,9 +579,17 @@ static int32_t qkv_projection_impl(const char* who, const uint16_t* x, int64_t l
   }
   const dim3 grid((unsigned)(8 * a.per_xcd)), block(GC::NT);
   const hipStream_t st = as_stream(stream);
-  if (app == kAppInt8) hipLaunchKernelGGL(qkv_gemm_kernel<kAppInt8>, grid, block, 0, st, a);
-  else if (app == kAppBf16) hipLaunchKernelGGL(qkv_gemm_kernel<kAppBf16>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(qkv_gemm_kernel<kAppNone>, grid, block, 0, st, a);
+  const bool vt = v_t != nullptr;
+  if (app == kAppInt8) {
+    if (vt) hipLaunchKernelGGL((qkv_gemm_kernel<kAppInt8, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((qkv_gemm_kernel<kAppInt8, false>), grid, block, 0, st, a);
+  } else if (app == kAppBf16) {
+    if (vt) hipLaunchKernelGGL((qkv_gemm_kernel<kAppBf16, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((qkv_gemm_kernel<kAppBf16, false>), grid, block, 0, st, a);
+  } else {
+    if (vt) hipLaunchKernelGGL((qkv_gemm_kernel<kAppNone, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((qkv_gemm_kernel<kAppNone, false>), grid, block, 0, st, a);
+  }
   if (int32_t e = check_launch(who)) return e;
   if (c) c->frames_written += n_frames;
   return ok();
@@ -554,14 +601,24 @@ extern "C" int32_t nomas_qkv_projection(const uint16_t* x, int64_t ld_x, int32_t
                                         int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
                                         void* stream) {
   return qkv_projection_impl("qkv_projection", x, ld_x, n_rows, hidden, w, ld_w, n_heads, head_dim, n_video,
-                             rope_table, qkv, ld_qkv, nullptr, stream);
+                             rope_table, qkv, ld_qkv, nullptr, 0, nullptr, stream);
+}
+
+extern "C" int32_t nomas_qkv_projection_vt(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
+                                           const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
+                                           int32_t n_video, const float* rope_table, uint16_t* qkv, int64_t ld_qkv,
+                                           uint16_t* v_t, int64_t ld_vt, void* stream) {
+  if (!v_t) return fail(NOMAS_E_INVALID, "qkv_projection_vt: v_t is NULL");
+  return qkv_projection_impl("qkv_projection_vt", x, ld_x, n_rows, hidden, w, ld_w, n_heads, head_dim, n_video,
+                             rope_table, qkv, ld_qkv, v_t, ld_vt, nullptr, stream);
 }
 
 extern "C" int32_t nomas_qkv_projection_append(const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
                                                const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,
                                                int32_t n_video, const float* rope_table, uint16_t* qkv,
-                                               int64_t ld_qkv, nomas_kvcache* c, void* stream) {
+                                               int64_t ld_qkv, uint16_t* v_t, int64_t ld_vt, nomas_kvcache* c,
+                                               void* stream) {
   if (!c) return fail(NOMAS_E_INVALID, "qkv_projection_append: cache descriptor is NULL");
   return qkv_projection_impl("qkv_projection_append", x, ld_x, n_rows, hidden, w, ld_w, n_heads, head_dim, n_video,
-                             rope_table, qkv, ld_qkv, c, stream);
+                             rope_table, qkv, ld_qkv, v_t, ld_vt, c, stream);
 }

@@ -89,7 +89,11 @@ def lib():
                                                  vp, sz, vp]),
         "nomas_block_causal_attention": (i32, [vp, vp, vp, i64, seg_p, i32, i32, i32, i32, i32, vp, i64, vp, f32,
                                                vp, sz, vp]),
-        "nomas_qkv_projection_append": (i32, [vp, i64, i32, i32, vp, i64, i32, i32, i32, vp, vp, i64, desc_p, vp]),
+        "nomas_qkv_projection_append": (i32, [vp, i64, i32, i32, vp, i64, i32, i32, i32, vp, vp, i64, vp, i64, desc_p,
+                                              vp]),
+        "nomas_qkv_projection_vt": (i32, [vp, i64, i32, i32, vp, i64, i32, i32, i32, vp, vp, i64, vp, i64, vp]),
+        "nomas_segment_attention_frames": (i32, [vp, vp, vp, i64, vp, i64, i32, i32, desc_p, i64, i32, vp, i64, vp, f32,
+                                                 i32, vp, sz, vp]),
         "nomas_segment_attention_noalloc_max_bytes": (sz, []),
         "nomas_segment_attention_noalloc": (i32, [vp, vp, vp, i64, i32, i32, desc_p, vp, i64, vp, f32, i32, vp]),
     }
@@ -283,6 +287,54 @@ def nomas_segment_attention_sparse(q, k_cur, v_cur, n_video, n_text, cache, bloc
                               workspace, stream)
 
 
+def nomas_segment_attention_frames(q, k_cur, v_cur, n_video, n_text, cache, first_frame, n_frames, v_t=None,
+                                   out=None, lse=None, softmax_scale=None, n_splits=0, workspace=None, stream=None):
+    """Attention against the retained frames [first_frame, first_frame + n_frames)
+    of ``cache`` and the current segment; with ``v_t`` (bf16 [H*D, ld_vt], the V^T
+    nomas_qkv_projection_vt writes) the values come from it and ``v_cur`` may be
+    None. Returns ``out``."""
+    d = cache.desc
+    H, D = d.n_heads, d.head_dim
+    n_q = n_video + n_text
+    qp, ld = _rows_view(q, "q", H, D)
+    kp, ldk = _rows_view(k_cur, "k_cur", H, D)
+    vp = None
+    if v_cur is not None:
+        vp, ldv = _rows_view(v_cur, "v_cur", H, D)
+        if ldv != ld or v_cur.shape[0] < n_q:
+            raise ValueError("v_cur must share q's row stride and hold n_video + n_text rows")
+    if ld != ldk:
+        raise ValueError("q, k_cur must share a row stride")
+    for t, name in ((q, "q"), (k_cur, "k_cur")):
+        if t.shape[0] < n_q:
+            raise ValueError(f"{name} holds fewer than n_video + n_text rows")
+    tp, ld_vt = None, 0
+    if v_t is not None:
+        if v_t.dtype != torch.bfloat16 or v_t.dim() != 2 or v_t.stride(1) != 1 or v_t.shape[0] != H * D:
+            raise ValueError(f"v_t must be a 2-D bfloat16 tensor [{H * D}, ld_vt] with unit inner stride")
+        tp, ld_vt = ctypes.c_void_p(v_t.data_ptr()), v_t.stride(0)
+    if out is None:
+        out = _on_stream(torch.empty((n_q, H, D), dtype=torch.bfloat16, device=q.device), stream)
+    op, ldo = _rows_view(out, "out", H, D)
+    if out.shape[0] < n_q:
+        raise ValueError("out holds fewer than n_video + n_text rows")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() < H * n_q:
+            raise ValueError("lse must be a contiguous float32 tensor of n_heads*n_q elements")
+        lp = ctypes.c_void_p(lse.data_ptr())
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if workspace is None:
+        nb = nomas_segment_attention_workspace_bytes(n_video, n_text, max(0, n_frames) * d.tokens_per_frame, H, D,
+                                                     d.kv_dtype, n_splits)
+        workspace = _on_stream(torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device), stream)
+    _check(lib().nomas_segment_attention_frames(qp, kp, vp, ld, tp, ld_vt, n_video, n_text, ctypes.byref(d),
+                                                int(first_frame), int(n_frames), op, ldo, lp, scale, n_splits,
+                                                ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                                _stream(stream)))
+    return out
+
+
 def nomas_segment_attention_noalloc_max_bytes():
     return lib().nomas_segment_attention_noalloc_max_bytes()
 
@@ -457,11 +509,20 @@ def nomas_rope3d_table(head_dim, t0, n_frames, grid_h, grid_w, band, theta=10000
     return table
 
 
-def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qkv=None, stream=None, cache=None):
+def new_vt(n_rows, n_heads, head_dim, device="cuda", stream=None):
+    """A V^T buffer for nomas_qkv_projection_vt: bf16 [H*D, round_up(n_rows, 128)]."""
+    return _on_stream(torch.empty((n_heads * head_dim, (n_rows + 127) // 128 * 128), dtype=torch.bfloat16,
+                                  device=device), stream)
+
+
+def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qkv=None, stream=None, cache=None,
+                         v_t=None):
     """qkv = [q | k | v] projection of x [n, hidden] by w [3*H*D, hidden] with RoPE
     on the video rows' q, k (when a table is given). Returns qkv [n, 3*H*D].
-    With ``cache`` (a KVCache): nomas_qkv_projection_append, which also appends
-    the n_video rows' keys and values to it."""
+    With ``v_t`` (bf16 [H*D, ld_vt]) the values are also written transposed
+    (nomas_qkv_projection_vt). With ``cache`` (a KVCache):
+    nomas_qkv_projection_append, which also appends the n_video rows' keys and
+    values to it."""
     for t, name in ((x, "x"), (w, "w")):
         if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
             raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor with unit inner stride")
@@ -481,15 +542,32 @@ def nomas_qkv_projection(x, w, n_heads, head_dim, n_video=0, rope_table=None, qk
         tp = ctypes.c_void_p(rope_table.data_ptr())
     args = (ctypes.c_void_p(x.data_ptr()), x.stride(0), n, hidden, ctypes.c_void_p(w.data_ptr()), w.stride(0),
             n_heads, head_dim, n_video, tp, ctypes.c_void_p(qkv.data_ptr()), qkv.stride(0))
-    if cache is None:
-        _check(lib().nomas_qkv_projection(*args, _stream(stream)))
+    vt_args = (None, 0)
+    if v_t is not None:
+        if v_t.dtype != torch.bfloat16 or v_t.dim() != 2 or v_t.stride(1) != 1 or v_t.shape[0] != n_heads * head_dim \
+                or v_t.shape[1] < n:
+            raise ValueError(f"v_t must be a 2-D bfloat16 tensor of [{n_heads * head_dim}, >= n] with unit inner stride")
+        vt_args = (ctypes.c_void_p(v_t.data_ptr()), v_t.stride(0))
+    if cache is not None:
+        _check(lib().nomas_qkv_projection_append(*args, *vt_args, ctypes.byref(cache.desc), _stream(stream)))
+    elif v_t is not None:
+        _check(lib().nomas_qkv_projection_vt(*args, *vt_args, _stream(stream)))
     else:
-        _check(lib().nomas_qkv_projection_append(*args, ctypes.byref(cache.desc), _stream(stream)))
+        _check(lib().nomas_qkv_projection(*args, _stream(stream)))
     return qkv
 
 
-def nomas_qkv_projection_append(x, w, n_heads, head_dim, n_video, rope_table, cache, qkv=None, stream=None):
-    """The final-step projection: nomas_qkv_projection that also appends the
-    n_video rows' keys and values to ``cache``. Returns qkv."""
+def nomas_qkv_projection_vt(x, w, n_heads, head_dim, n_video, rope_table, v_t, qkv=None, stream=None):
+    """nomas_qkv_projection that also writes the values transposed into ``v_t``
+    (see new_vt). Returns qkv."""
     return nomas_qkv_projection(x, w, n_heads, head_dim, n_video=n_video, rope_table=rope_table, qkv=qkv,
-                                stream=stream, cache=cache)
+                                stream=stream, v_t=v_t)
+
+
+def nomas_qkv_projection_append(x, w, n_heads, head_dim, n_video, rope_table, cache, qkv=None, stream=None,
+                                v_t=None):
+    """The final-step projection: nomas_qkv_projection that also appends the
+    n_video rows' keys and values to ``cache`` (and, with ``v_t``, writes the
+    values transposed). Returns qkv."""
+    return nomas_qkv_projection(x, w, n_heads, head_dim, n_video=n_video, rope_table=rope_table, qkv=qkv,
+                                stream=stream, cache=cache, v_t=v_t)

@@ -329,9 +329,48 @@ def test_projection_append_rejects_before_launch_and_keeps_descriptor():
     assert rc == 0
     p = ctypes.c_void_p(1 << 24)
     def call(H=2, D=64, nv=48, desc=d):
-        return L.nomas_qkv_projection_append(p, 128, 64, 128, p, 128, H, D, nv, None, p, 384, desc, None)
+        return L.nomas_qkv_projection_append(p, 128, 64, 128, p, 128, H, D, nv, None, p, 384, None, 0, desc, None)
     assert call(H=3) == nomas.NOMAS_E_INVALID and b"heads" in L.nomas_last_error()
     assert call(nv=40) == nomas.NOMAS_E_INVALID and b"multiple" in L.nomas_last_error()
     assert call(nv=0) == nomas.NOMAS_E_INVALID
     assert call(desc=None) == nomas.NOMAS_E_INVALID
     assert d.frames_written == 0
+
+
+def test_projection_vt_rejects_bad_transposed_output():
+    L = nomas.lib()
+    p = ctypes.c_void_p(1 << 24)
+    def call(vt=p, ld_vt=64, n=64):
+        return L.nomas_qkv_projection_vt(p, 128, n, 128, p, 128, 2, 64, 0, None, p, 384, vt, ld_vt, None)
+    assert call(vt=None) == nomas.NOMAS_E_INVALID
+    assert call(vt=ctypes.c_void_p((1 << 24) + 8)) == nomas.NOMAS_E_INVALID and b"v_t" in L.nomas_last_error()
+    assert call(ld_vt=56) == nomas.NOMAS_E_INVALID      # fewer columns than rows
+    assert call(ld_vt=68) == nomas.NOMAS_E_INVALID      # not a multiple of 8
+    L2, d, rc = _desc(dtype=1, heads=2, dim=64, tpf=24, cap=4)
+    assert L2.nomas_qkv_projection_append(p, 128, 64, 128, p, 128, 2, 64, 48, None, p, 384, p, 60, ctypes.byref(d),
+                                          None) == nomas.NOMAS_E_INVALID
+    assert d.frames_written == 0
+
+
+def test_attention_frames_rejects_frames_not_retained():
+    """Frame ranges outside the retained frames, a missing value input and a bad
+    V^T are refused before anything is enqueued; the descriptor is unchanged."""
+    L, d, rc = _desc(dtype=1, heads=2, dim=64, tpf=24, cap=4)
+    assert rc == 0
+    d.frames_written = 6                                   # retained: frames [2, 6)
+    p = ctypes.c_void_p(1 << 24)
+    ws = ctypes.c_void_p(1 << 26)
+    def call(first, n, v=p, vt=None, ld_vt=0):
+        return L.nomas_segment_attention_frames(p, p, v, 384, vt, ld_vt, 48, 16, ctypes.byref(d), first, n, p, 128,
+                                                None, ctypes.c_float(0.125), 0, ws, 1 << 30, None)
+    assert call(1, 3) == nomas.NOMAS_E_INVALID and b"retained" in L.nomas_last_error()
+    assert call(3, 4) == nomas.NOMAS_E_INVALID            # runs past frames_written
+    assert call(2, -1) == nomas.NOMAS_E_INVALID
+    assert call(2, 4, v=None) == nomas.NOMAS_E_INVALID    # neither v_cur nor v_t
+    assert call(2, 4, v=None, vt=p, ld_vt=64) == nomas.NOMAS_E_INVALID   # below round_up(n_q = 64, 128)
+    assert call(2, 4, v=None, vt=p, ld_vt=132) == nomas.NOMAS_E_INVALID  # not a multiple of 8
+    assert call(2, 4, v=None, vt=ctypes.c_void_p((1 << 24) + 2), ld_vt=128) == nomas.NOMAS_E_INVALID
+    small = L.nomas_segment_attention_frames(p, p, p, 384, None, 0, 48, 16, ctypes.byref(d), 3, 2, p, 128, None,
+                                             ctypes.c_float(0.125), 0, ws, 64, None)
+    assert small == nomas.NOMAS_E_WORKSPACE
+    assert d.frames_written == 6

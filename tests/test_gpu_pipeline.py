@@ -80,3 +80,71 @@ def test_projection_attention_append_chain(int8):
         else:
             got_k, got_v = synth.bf16_bits_to_f64(kc[slot:slot + tpf]), synth.bf16_bits_to_f64(vc[slot:slot + tpf])
         assert np.array_equal(got_k, kf) and np.array_equal(got_v, vf)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_fused_final_step_chain(int8):
+    """The chain with the fused calls: every denoising step projects with the
+    values also written transposed (nomas_qkv_projection_vt) and attends with
+    them to the window of W frames before the segment
+    (nomas_segment_attention_frames); the final step's projection also writes the
+    segment into the cache (nomas_qkv_projection_append), which has room for
+    W + F frames, so its attention still sees the frames the segment will evict
+    from the window. Four segments of two steps each (different inputs per
+    step); the fourth segment's window wraps round the ring. Checked: V^T
+    equals the projection's value channels bit for bit; each step's attention against the oracle over the ring model's window; the
+    cache, slot by slot, against the oracle quantiser and a ring model of
+    capacity W + F fed with the final steps' keys and values."""
+    H, D, hidden, gh, gw, F, T, W = 2, 128, 256, 4, 8, 2, 24, 3
+    tpf, nv = gh * gw, F * gh * gw
+    n = nv + T
+    band = (32, 48, 48)
+    rng = np.random.default_rng(23)
+    wb = synth._round_bf16_bits((rng.standard_normal((3 * H * D, hidden)) / math.sqrt(hidden)).astype(np.float32))
+    w = dev_bf16(wb)
+    cache = nomas.KVCache(H, D, tpf, W + F, int8)
+    ring = RingModel(W + F)
+    for s in range(4):          # the last segment's window wraps round the ring
+        t0 = F * s
+        table = nomas.nomas_rope3d_table(D, t0, F, gh, gw, band)
+        before = cache.frames_written
+        first, n_win = max(0, before - W), min(W, before)
+        for step in range(2):
+            final = step == 1
+            say(f"fused chain: int8={int8} segment {s} step {step}")
+            xb = synth.normal_bf16((n, 1, hidden), 98, s, step, 0)[:, 0]
+            vt = nomas.new_vt(n, H, D)
+            if final:
+                y = nomas.nomas_qkv_projection_append(dev_bf16(xb), w, H, D, nv, table, cache, v_t=vt)
+            else:
+                y = nomas.nomas_qkv_projection_vt(dev_bf16(xb), w, H, D, nv, table, vt)
+            q, k = y[:, :H * D], y[:, H * D:2 * H * D]
+            out = nomas.nomas_segment_attention_frames(q, k, None, nv, T, cache, first, n_win, v_t=vt)
+            torch.cuda.synchronize()
+            got_qkv = host_f64(y)
+            assert torch.equal(vt[:, :n], y[:, 2 * H * D:].t()), "V^T differs from the value channels"
+            gq, gk, gv = (got_qkv[:, i * H * D:(i + 1) * H * D].reshape(n, H, D) for i in range(3))
+            win = [p for f, p in ring.retained() if first <= f < first + n_win]
+            kp = np.concatenate([p[0] for p in win], 0) if win else None
+            vp = np.concatenate([p[1] for p in win], 0) if win else None
+            ref, _ = attention.segment_attention(gq, gk, gv, kp, vp, 1 / math.sqrt(D))
+            diff = np.abs(host_f64(out) - ref)
+            assert diff.max() <= 1e-2 * np.abs(ref).max() and diff.mean() <= 1e-3, (s, step, diff.max())
+            if final:
+                fr = []
+                for f in range(F):
+                    kf, vf = gk[f * tpf:(f + 1) * tpf], gv[f * tpf:(f + 1) * tpf]
+                    if int8:
+                        kf, vf = quant.dequantise(*quant.quantise(kf)), quant.dequantise(*quant.quantise(vf))
+                    fr.append((kf, vf))
+                ring.append(fr)
+        assert cache.frames_written == ring.frames_written == before + F
+    kc, vc, ks, vs = cache_slots(cache)
+    for f, (kf, vf) in ring.retained():
+        slot = (f % (W + F)) * tpf
+        if int8:
+            got_k = kc[slot:slot + tpf].astype(np.float64) * ks[slot:slot + tpf, :, None]
+            got_v = vc[slot:slot + tpf].astype(np.float64) * vs[slot:slot + tpf, :, None]
+        else:
+            got_k, got_v = synth.bf16_bits_to_f64(kc[slot:slot + tpf]), synth.bf16_bits_to_f64(vc[slot:slot + tpf])
+        assert np.array_equal(got_k, kf) and np.array_equal(got_v, vf)

@@ -184,3 +184,30 @@ def test_projection_append_equals_projection_then_append(case, int8):
         else:
             kf, vf = p
             assert np.array_equal(synth.bf16_bits_to_f64(kc[sl]), kf) and np.array_equal(synth.bf16_bits_to_f64(vc[sl]), vf)
+
+
+@pytest.mark.parametrize("case", [
+    # H, D, hidden, n_video, n_text
+    (1, 64, 128, 48, 29),        # one head: the value part starts inside a block; 77 rows (ragged run)
+    (3, 64, 192, 96, 5),         # odd head count
+    (2, 128, 256, 128, 0),       # whole 16-token runs only
+    (16, 128, 2048, 7680, 256),  # the layer shape
+], ids=["h1", "h3", "runs", "layer"])
+def test_projection_vt_is_the_value_channels_transposed(case):
+    """nomas_qkv_projection_vt writes qkv bit for bit as nomas_qkv_projection and
+    V^T equal to its value channels transposed; columns past n_rows keep the
+    sentinel they held."""
+    H, D, hidden, nv, nt = case
+    n = nv + nt
+    xb, wb = _data(n, hidden, 3 * H * D, seed=H + D)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    table = nomas.nomas_rope3d_table(D, 2, max(1, nv // 16), 4, 4, (D // 4, 3 * D // 8, 3 * D // 8)) if nv else None
+    say(f"qkv vt: H={H} D={D} n={n}")
+    vt = nomas.new_vt(n, H, D)
+    vt.view(torch.int16).fill_(0x7FC1)
+    y_vt = nomas.nomas_qkv_projection_vt(x, w, H, D, nv, table, vt)
+    y = nomas.nomas_qkv_projection(x, w, H, D, n_video=nv, rope_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(y_vt, y)
+    assert torch.equal(vt[:, :n], y[:, 2 * H * D:].t())
+    assert bool((vt[:, n:].view(torch.int16) == 0x7FC1).all()), "columns past n_rows were written"

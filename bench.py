@@ -18,6 +18,10 @@ Also reported (outside the timed steps):
     ``archive_h2d_gbps``;
   * the fused QKV projection + RoPE of the layer (7,936 x 2,048 -> 6,144)
     -> ``qkv_tflops``;
+  * one layer's projection + attention (+ append) at the INT8 layer shape,
+    unfused and through the fused calls (projection writing V^T and, at the
+    final step, the cache; attention reading V^T and the frames before the
+    segment) -> ``chain_turn_ms_per_layer_unfused`` / ``_fused``;
   * the layer shape under the sparse policy: selection of 34 of the 135
     candidate blocks + sparse attention -> ``sparse_select_us``,
     ``sparse_attention_ms``;
@@ -35,8 +39,9 @@ Also reported (outside the timed steps):
   * the fp64 oracle on a bounded sample of query rows -> ``cpu_baseline`` (all the
     BLAS threads), and on one thread over a sample cut by the thread count
     -> ``cpu_baseline.one_thread``.
-``--headline-only`` times the single-layer step and nothing else, so a kernel
-trace of that run holds only the headline's launches.
+``--headline-only`` times the single-layer step and nothing else (no clock
+sampling either), so a kernel trace of that run holds only the headline's
+launches.
 Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
 
@@ -119,14 +124,16 @@ def layer_step_bench(args):
     wall = time.perf_counter() - t0
     # the graphics clock under this load: the same attention launches repeated
     # for a few seconds while amd-smi is sampled (the timed steps above last
-    # well under the sampling period)
+    # well under the sampling period); not in --headline-only runs, whose kernel
+    # trace is to hold the timed steps' launches alone
     clk = ClockSampler()
-    with clk:
-        t_end = time.perf_counter() + 3.0
-        while time.perf_counter() < t_end:
-            for _ in range(20):
-                nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
-            torch.cuda.synchronize()
+    if not args.headline_only:
+        with clk:
+            t_end = time.perf_counter() + 3.0
+            while time.perf_counter() < t_end:
+                for _ in range(20):
+                    nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
+                torch.cuda.synchronize()
     rope_ms = [e[0].elapsed_time(e[1]) for e in ev]
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
     app_ms = [e[2].elapsed_time(e[3]) for e in ev]
@@ -466,6 +473,67 @@ def qkv_bench(reps=20):
     return dict(qkv_us=round(ms * 1e3, 2), qkv_tflops=round(flop / ms / 1e9, 1))
 
 
+def fused_chain_bench(reps=10):
+    """One layer's QKV projection + attention (+ the segment's append at the
+    final step) at the INT8 layer shape (16x128 heads, 18-frame window of 24x40,
+    8-frame segment + 256 text, hidden 2,048), unfused and fused. Unfused: the
+    projection, attention on its views (values transposed inside the call), and
+    at the final step the quantise-append. Fused: the projection also writes
+    V^T (nomas_qkv_projection_vt; at the final step nomas_qkv_projection_append,
+    which also writes the segment into a cache of 18 + 8 frames) and attention
+    reads V^T and the 18 frames before the segment
+    (nomas_segment_attention_frames). A turn is 7 steps + the final one."""
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = synth.WORKLOADS["layer_int8"]
+    H, D, F, W, hidden = wl.n_heads, wl.head_dim, wl.seg_frames, wl.capacity_frames, H_HIDDEN
+    nv, nt, n = wl.n_video, wl.n_text, wl.n_q
+    kb, vb = synth.prefill_kv(wl)
+    plain = nomas.KVCache(H, D, wl.tpf, W, True)
+    plain.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    roomy = nomas.KVCache(H, D, wl.tpf, W + F, True)
+    roomy.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    x = dev_bf16(synth.normal_bf16((n, 1, hidden), 79, 1, 0, 0)[:, 0])
+    w = torch.randn((3 * H * D, hidden), device="cuda", dtype=torch.float32).div_(math.sqrt(hidden)).to(torch.bfloat16)
+    table = nomas.nomas_rope3d_table(D, wl.t0, F, wl.grid_h, wl.grid_w, wl.rope_split)
+    y = torch.empty((n, 3 * H * D), dtype=torch.bfloat16, device="cuda")
+    vt = nomas.new_vt(n, H, D)
+    out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+    q, k, v = (y[:, i * H * D:(i + 1) * H * D] for i in range(3))
+    ws = nomas.workspace_for(plain, nv, nt)
+
+    def unfused(final):
+        nomas.nomas_qkv_projection(x, w, H, D, n_video=nv, rope_table=table, qkv=y)
+        nomas.nomas_segment_attention(q, k, v, nv, nt, plain, out=out, workspace=ws)
+        if final:
+            plain.nomas_kvcache_append(k, v, F)
+
+    def fused(final):
+        if final:
+            nomas.nomas_qkv_projection_append(x, w, H, D, nv, table, roomy, qkv=y, v_t=vt)
+            first = roomy.frames_written - F - W
+        else:
+            nomas.nomas_qkv_projection_vt(x, w, H, D, nv, table, vt, qkv=y)
+            first = roomy.frames_written - W
+        nomas.nomas_segment_attention_frames(q, k, None, nv, nt, roomy, first, W, v_t=vt, out=out, workspace=ws)
+
+    t = {}
+    for name, fn in (("unfused_step", lambda: unfused(False)), ("unfused_final", lambda: unfused(True)),
+                     ("fused_step", lambda: fused(False)), ("fused_final", lambda: fused(True))):
+        t[name] = time_launches(fn, reps)
+    t["qkv_vt"] = time_launches(lambda: nomas.nomas_qkv_projection_vt(x, w, H, D, nv, table, vt, qkv=y), reps)
+    turn_u = 7 * t["unfused_step"] + t["unfused_final"]
+    turn_f = 7 * t["fused_step"] + t["fused_final"]
+    log(f"[bench] fused chain (INT8 layer): step {t['unfused_step']:.3f} -> {t['fused_step']:.3f} ms, final step "
+        f"{t['unfused_final']:.3f} -> {t['fused_final']:.3f} ms, turn per layer {turn_u:.3f} -> {turn_f:.3f} ms; "
+        f"projection with V^T {t['qkv_vt'] * 1e3:.1f} us")
+    return dict(chain_step_ms_unfused=round(t["unfused_step"], 4), chain_step_ms_fused=round(t["fused_step"], 4),
+                chain_final_ms_unfused=round(t["unfused_final"], 4), chain_final_ms_fused=round(t["fused_final"], 4),
+                chain_turn_ms_per_layer_unfused=round(turn_u, 4), chain_turn_ms_per_layer_fused=round(turn_f, 4),
+                qkv_vt_us=round(t["qkv_vt"] * 1e3, 2))
+
+
 def archive_bench(reps=10):
     """Host archive of evicted frames: one INT8 layer window (18 frames of the
     24x40 grid, 16x128 heads); the 8 frames a segment evicts are exported to
@@ -643,6 +711,7 @@ def main():
         extra.update(sparse_layer_bench())
         extra.update(archive_bench())
         extra.update(qkv_bench())
+        extra.update(fused_chain_bench())
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_rows)
     line = {
         "metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)",

@@ -409,6 +409,30 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       }
     }
   };
+  // the last, partial key tile of the current segment (or of a range of the
+  // joint sequence): its rows past the end must not be fetched at all, and the
+  // scalar offset of a buffer load lies outside the range check, so the tile
+  // gets a descriptor based at its first row and bounded by its valid rows
+  auto start_k_tail = [&](int t) {
+    int key0, nvalid;
+    tile_info(t, std::false_type{}, key0, nvalid);
+    key0 = __builtin_amdgcn_readfirstlane(key0);
+    nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+    const uint64_t base = reinterpret_cast<uint64_t>(a.kcur + (int64_t)key0 * a.ld_qkv + (int64_t)h * D);
+    const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base & 0xffffffffu)));
+    const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(base >> 32)));
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(lo | (hi << 32)), (short)0, (int)(nvalid * a.ld_qkv * 2), 0x00020000);
+    const int kstride = (int)a.ld_qkv * 2;
+    unsigned char* Ks = kbuf(0);
+#pragma unroll
+    for (int k = 0; k < C::KI; ++k) {
+      const int blk = wave * C::KI + k, p = blk * 64 + lane;
+      const int row = p / C::KC, c = (p % C::KC) ^ swz_k<D>(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + blk * 1024), 16,
+                                               row * kstride + c * 16, 0, 0, 0);
+    }
+  };
   auto start_v = [&](int t, int i, auto ct) {
     constexpr bool cache = decltype(ct)::value;
     int key0, nvalid;
@@ -849,7 +873,8 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     const std::bool_constant<I8 && decltype(ct)::value> scaled_tag;
     int key0, nvalid, klo;
     tile_rows(t, ct, key0, nvalid, klo);
-    start_k(t, 0, ct);
+    if constexpr (decltype(ct)::value) start_k(t, 0, ct);   // cache tiles read inside the head's rows
+    else start_k_tail(t);
     start_v(t, 0, ct);
     wait_copies();
     finish_k(t, 0, ct);

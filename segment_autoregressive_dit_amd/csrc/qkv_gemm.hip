@@ -130,6 +130,9 @@ __device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][
   constexpr int ES = I8 ? 1 : 2;                       // bytes per cached element
   constexpr int WM = 16 * TI;                          // the wave's channels (64)
   constexpr int CH = WN / 16;                          // 16-token runs per channel row
+  static_assert(WM == 64, "a wave's channels are one head (D 64) or half of one (D 128, partner wave ^ 1)");
+  static_assert(GC::NW * WM * WN * 2 <= GC::S * (GC::WBYTES + GC::XBYTES), "bf16 staging fits the operand ring");
+  static_assert((GC::BM / WM) % 2 == 0, "partner waves (wave ^ 1) hold the two channel halves of a 128-wide head");
   const int G = lane >> 4, i16 = lane & 15;
   const int D = a.head_dim;
   const int part = c0 < a.n_ch ? c0 / a.hd : 3;        // 1: keys, 2: values

@@ -184,3 +184,83 @@ def test_cached_attention_medium_shapes_sampled_rows(i):
     x = [synth.bf16_bits_to_f64(t) for t in (q, k, v)]
     ref, _ = attention.segment_attention(x[0][rows], x[1], x[2], kp, vp, 1.0 / math.sqrt(D))
     _check(host_f64(out)[rows], ref, f"medium case {i}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_frame_range_random(i):
+    """nomas_segment_attention_frames over a random range of the retained frames
+    of a cache built by random appends (wrapping or not), values row-major or as
+    V^T with NaN past n_q, against the oracle over the ring model's frames."""
+    r = np.random.default_rng([2032, i])
+    H, D = int(r.choice([1, 2, 3])), int(r.choice([64, 128]))
+    gh, gw = int(r.integers(1, 9)), int(r.integers(1, 11))
+    tpf, cap = gh * gw, int(r.integers(1, 8))
+    int8 = bool(r.integers(0, 2))
+    appends = [int(r.integers(1, cap + 2)) for _ in range(int(r.integers(1, 5)))]
+    cache = nomas.KVCache(H, D, tpf, cap, int8)
+    ring = RingModel(cap)
+    for a, n in enumerate(appends):
+        kb = synth.normal_bf16((n * tpf, H, D), 700 + i, a, 0, 3)
+        vb = synth.normal_bf16((n * tpf, H, D), 700 + i, a, 0, 4)
+        cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), n)
+        ring.append([(kb[f * tpf:(f + 1) * tpf], vb[f * tpf:(f + 1) * tpf]) for f in range(n)])
+    fw, valid = ring.frames_written, ring.valid_frames()
+    n_frames = int(r.integers(0, valid + 1))
+    first = int(r.integers(fw - valid, fw - n_frames + 1))
+    nv, nt = int(r.integers(0, 3)) * tpf, int(r.integers(0, 150))
+    if nv + nt == 0:
+        nt = 1
+    n_q = nv + nt
+    splits = int(r.choice([0, 1, 2, 3, 5]))
+    use_vt = bool(r.integers(0, 2))
+    say(f"fuzz frames {i}: H={H} D={D} tpf={tpf} cap={cap} appends={appends} int8={int8} range=[{first}, "
+        f"{first + n_frames}) nv={nv} nt={nt} splits={splits} vt={use_vt}")
+    q, k, v = (synth.normal_bf16((n_q, H, D), 700 + i, 9, 0, t) for t in range(3))
+    vd = dev_bf16(v)
+    vt = None
+    if use_vt:
+        vt = torch.full((H * D, (n_q + 127) // 128 * 128 + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vt[:, :n_q] = vd.reshape(n_q, H * D).t()
+    lse = torch.empty(H * n_q, dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention_frames(dev_bf16(q), dev_bf16(k), None if use_vt else vd, nv, nt, cache,
+                                               first, n_frames, v_t=vt, lse=lse, n_splits=splits)
+    torch.cuda.synchronize()
+    win = [p for f, p in ring.retained() if first <= f < first + n_frames]
+    kp = vp = None
+    if win:
+        kp = np.concatenate([synth.bf16_bits_to_f64(p[0]) for p in win], 0)
+        vp = np.concatenate([synth.bf16_bits_to_f64(p[1]) for p in win], 0)
+        if int8:
+            kp, vp = quant.dequantise(*quant.quantise(kp)), quant.dequantise(*quant.quantise(vp))
+    x = [synth.bf16_bits_to_f64(t) for t in (q, k, v)]
+    ref, ref_lse = attention.segment_attention(x[0], x[1], x[2], kp, vp, 1.0 / math.sqrt(D))
+    _check(host_f64(out), ref, f"frames case {i}")
+    assert np.max(np.abs(lse.cpu().numpy().reshape(H, -1) - ref_lse)) <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_fused_projection_random(i):
+    """The final-step projection (with V^T) on random shapes and cache states:
+    qkv bitwise the plain projection's, the cache byte for byte the plain
+    projection + nomas_kvcache_append, V^T the value channels transposed."""
+    import test_gpu_qkv as QK
+    r = np.random.default_rng([2033, i])
+    H, D = int(r.integers(1, 5)), int(r.choice([64, 128]))
+    hidden = int(r.choice([64, 128, 256]))
+    gh, gw = int(r.integers(1, 7)), int(r.integers(1, 9))
+    F, T = int(r.integers(1, 4)), int(r.integers(0, 120))
+    cap = int(r.integers(1, 6))
+    prior = int(r.integers(0, 2 * cap + 1))
+    int8 = bool(r.integers(0, 2))
+    say(f"fuzz fused projection {i}: H={H} D={D} hidden={hidden} grid={gh}x{gw} F={F} T={T} cap={cap} "
+        f"prior={prior} int8={int8}")
+    y_fused, y_plain, caches, ring, tpf, vt = QK._fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior,
+                                                             seed=800 + i, with_vt=True)
+    assert torch.equal(y_fused, y_plain)
+    for name in ("k", "v", "k_scale", "v_scale"):
+        a, b = getattr(caches[0], name), getattr(caches[1], name)
+        if a is not None:
+            assert torch.equal(a, b), f"cache {name} differs"
+    assert caches[0].frames_written == caches[1].frames_written == ring.frames_written
+    n = F * tpf + T
+    assert torch.equal(vt[:, :n], y_plain[:, 2 * H * D:].t())

@@ -105,12 +105,12 @@ def test_table_matches_rope_kernel():
     assert torch.equal(y[:, :hidden].reshape(n, H, D), q)
 
 
-def _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed):
+def _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed, with_vt=False):
     """Run the final-step projection into a ring cache that already holds
     ``prior`` frames; return (qkv of the fused call, qkv of the plain call,
-    fused cache, cache filled by the plain projection + nomas_kvcache_append,
+    [fused cache, cache filled by the plain projection + nomas_kvcache_append],
     the ring model of the fused cache with the oracle's quantisation of the
-    stored K/V rows)."""
+    stored K/V rows, tokens per frame, the fused call's V^T or None)."""
     from oracle import quant
     from oracle.ring import RingModel
     tpf = gh * gw
@@ -134,7 +134,11 @@ def _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed):
             c.nomas_kvcache_append(dev_bf16(kp), dev_bf16(vp), prior)
         ring.append([None] * prior)
     say(f"qkv fused append: H={H} D={D} tpf={tpf} F={F} cap={cap} int8={int8} prior={prior}")
-    y_fused = nomas.nomas_qkv_projection_append(x, w, H, D, nv, table, caches[0])
+    vt = None
+    if with_vt:
+        vt = nomas.new_vt(n, H, D)
+        vt.view(torch.int16).fill_(0x7FC1)
+    y_fused = nomas.nomas_qkv_projection_append(x, w, H, D, nv, table, caches[0], v_t=vt)
     y_plain = nomas.nomas_qkv_projection(x, w, H, D, n_video=nv, rope_table=table)
     caches[1].nomas_kvcache_append(y_plain[:, H * D:2 * H * D], y_plain[:, 2 * H * D:], F)
     torch.cuda.synchronize()
@@ -145,7 +149,9 @@ def _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed):
         kf, vf = kv[f * tpf:(f + 1) * tpf, 1], kv[f * tpf:(f + 1) * tpf, 2]
         frames.append((quant.quantise(kf), quant.quantise(vf)) if int8 else (kf, vf))
     ring.append(frames)
-    return y_fused, y_plain, caches, ring, tpf
+    if with_vt:
+        assert bool((vt[:, n:].view(torch.int16) == 0x7FC1).all()), "V^T columns past n_rows were written"
+    return y_fused, y_plain, caches, ring, tpf, vt
 
 
 @pytest.mark.parametrize("int8", [False, True])
@@ -164,7 +170,7 @@ def test_projection_append_equals_projection_then_append(case, int8):
     ring model's slots; frames_written as the ring model's."""
     from _gpu_util import cache_slots
     H, D, hidden, gh, gw, F, T, cap, prior = case
-    y_fused, y_plain, caches, ring, tpf = _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed=3 + F)
+    y_fused, y_plain, caches, ring, tpf, _ = _fused_case(H, D, hidden, gh, gw, F, T, cap, int8, prior, seed=3 + F)
     assert torch.equal(y_fused, y_plain), "the fused call's qkv differs from the plain projection's"
     for name in ("k", "v", "k_scale", "v_scale"):
         a, b = getattr(caches[0], name), getattr(caches[1], name)

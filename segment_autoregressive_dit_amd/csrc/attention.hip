@@ -305,10 +305,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
     for (int db = 0; db < D / 16; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- buffer descriptors: the range check returns zeros for rows past the
-  // attended cache tokens / the current segment (rows of a partial tile inside
-  // the range that are not attended are masked like those past it).
-  const int c_end = a.c_a0 + a.c_na;   // one past the last physical cache row read
+  // ---- buffer descriptors. The range check covers a load's per-lane offset,
+  // not its scalar (tile) offset, so what keeps every read in bounds is the
+  // tile walk: cache tiles read rows inside the head's token_pitch rows, full
+  // current tiles lie inside the segment, and its partial tail gets a
+  // descriptor of its own (start_k_tail). Rows of a partial tile outside its
+  // valid rows may hold anything and are masked (logits) and zeroed (values).
+  const int c_end = a.c_a0 + a.c_na;   // one past the last physical cache row attended
   const __amdgpu_buffer_rsrc_t rk_c = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<char*>(const_cast<void*>(a.kc)) + (int64_t)h * a.pitch_c * D * ES, (short)0, c_end * D * ES, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv_c = __builtin_amdgcn_make_buffer_rsrc(
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   const __amdgpu_buffer_rsrc_t rv_n = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.vtcur) + (int64_t)h * D * a.pitch_cur, (short)0, D * a.pitch_cur * 2, 0x00020000);
 
-  // per-key scales of the attended cache tokens (zeros past the range)
+  // per-key scales of the attended cache tokens
   const __amdgpu_buffer_rsrc_t rks_c = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(a.ks) + (int64_t)h * a.pitch_c, (short)0, I8 ? c_end * 4 : 0, 0x00020000);
   const __amdgpu_buffer_rsrc_t rvs_c = __builtin_amdgcn_make_buffer_rsrc(

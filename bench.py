@@ -41,7 +41,8 @@ Also reported (outside the timed steps):
     -> ``cpu_baseline.one_thread``.
 ``--headline-only`` times the single-layer step and nothing else (no clock
 sampling either), so a kernel trace of that run holds only the headline's
-launches.
+launches. ``--config 1|3|4|5`` prints one line for that workload alone (tiny,
+single-layer INT8, full history, the denoise sweep); 2 is the default line.
 Inputs are seeded synthetic N(0,1) bf16 tensors already resident in HBM.
 """
 
@@ -78,6 +79,10 @@ def parse():
                    help="time the single-layer step only (no extra measurements): a kernel trace of this run "
                         "holds the headline attention launches alone")
     p.add_argument("--cpu-rows", type=int, default=7936, help="query rows per head in the CPU sample")
+    p.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5], default=2,
+                   help="the workload of the line: 1 tiny (correctness shape), 2 single layer bf16 (default, with "
+                        "every extra measurement), 3 single layer INT8 (+ quantise-append), 4 full history "
+                        "(split-KV sweep), 5 the 54-layer INT8 denoise sweep")
     return p.parse_args()
 
 
@@ -238,11 +243,28 @@ def time_launches(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def time_calls(fn, reps):
+    """Median GPU time (ms) of one call of ``fn`` over ``reps`` back-to-back
+    calls, HIP events recorded between them on the current stream, for calls
+    far longer than the host's launch cost (the timed step's own method)."""
+    import torch
+    for _ in range(3):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+
+
 def layer_int8_bench(reps=20):
     """The single-layer shape with an INT8 window (16x128 heads, 18 frames of
-    24x40, 4 outlier key channels per head at 20x): the attention launch and the
-    quantise-append of the 8-frame segment, each timed on its own with HIP
-    events."""
+    24x40, 4 outlier key channels per head at 20x): the attention call (median
+    of back-to-back calls, HIP events between them) and the quantise-append of
+    the 8-frame segment (batches behind a spin kernel), each on its own."""
     import torch
     from segment_autoregressive_dit_amd import nomas, synth
 
@@ -256,7 +278,9 @@ def layer_int8_bench(reps=20):
     ws = nomas.workspace_for(cache, wl.n_video, wl.n_text)
     attn = lambda: nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out, workspace=ws)
     app = lambda: cache.nomas_kvcache_append(k, v, F)
-    res = {"attention": time_launches(attn, reps), "append": time_launches(app, 5 * reps)}
+    # attention as in the timed step (a call lasts ~1.5 ms, far beyond the
+    # host's launch cost); the short append in batches behind a spin kernel
+    res = {"attention": time_calls(attn, reps), "append": time_launches(app, 5 * reps)}
     flop = wl.attention_flop()
     # read K, V bf16 + write K, V codes + one fp32 scale per (token, head) each
     app_bytes = 2 * wl.n_video * H * D * 2 + 2 * wl.n_video * H * D + 2 * wl.n_video * H * 4
@@ -445,7 +469,7 @@ def sparse_layer_bench(reps=20):
     sel = lambda: nomas.nomas_sparse_select(q, wl.n_q, cache, n_sel, block_list=lists, workspace=ws_sel)
     att = lambda: nomas.nomas_segment_attention_sparse(q, k, v, wl.n_video, wl.n_text, cache, lists, out=out,
                                                        workspace=ws)
-    times = {"select": time_launches(sel, reps), "attention": time_launches(att, reps)}
+    times = {"select": time_launches(sel, reps), "attention": time_calls(att, reps)}
     flop = 4 * wl.n_q * (n_sel * 128 + wl.n_q) * D * H
     log(f"[bench] sparse layer: select {times['select'] * 1e3:.1f} us, attention {times['attention']:.3f} ms "
         f"({flop / times['attention'] / 1e9:.1f} TFLOP/s on the kept keys)")
@@ -467,7 +491,7 @@ def qkv_bench(reps=20):
     y = torch.empty((wl.n_q, 3 * H * D), dtype=torch.bfloat16, device="cuda")
     table = nomas.nomas_rope3d_table(D, wl.t0, wl.seg_frames, wl.grid_h, wl.grid_w, wl.rope_split)
     fn = lambda: nomas.nomas_qkv_projection(x, w, H, D, n_video=wl.n_video, rope_table=table, qkv=y)
-    ms = time_launches(fn, reps)
+    ms = time_calls(fn, reps)
     flop = 2 * wl.n_q * hidden * 3 * H * D
     log(f"[bench] qkv projection + RoPE: {ms * 1e3:.1f} us, {flop / ms / 1e9:.1f} TFLOP/s")
     return dict(qkv_us=round(ms * 1e3, 2), qkv_tflops=round(flop / ms / 1e9, 1))
@@ -521,8 +545,8 @@ def fused_chain_bench(reps=10):
     t = {}
     for name, fn in (("unfused_step", lambda: unfused(False)), ("unfused_final", lambda: unfused(True)),
                      ("fused_step", lambda: fused(False)), ("fused_final", lambda: fused(True))):
-        t[name] = time_launches(fn, reps)
-    t["qkv_vt"] = time_launches(lambda: nomas.nomas_qkv_projection_vt(x, w, H, D, nv, table, vt, qkv=y), reps)
+        t[name] = time_calls(fn, reps)
+    t["qkv_vt"] = time_calls(lambda: nomas.nomas_qkv_projection_vt(x, w, H, D, nv, table, vt, qkv=y), reps)
     turn_u = 7 * t["unfused_step"] + t["unfused_final"]
     turn_f = 7 * t["fused_step"] + t["fused_final"]
     log(f"[bench] fused chain (INT8 layer): step {t['unfused_step']:.3f} -> {t['fused_step']:.3f} ms, final step "
@@ -664,6 +688,48 @@ def traffic_per_launch():
         return None
 
 
+def single_config(args):
+    """One JSON line for workload 1, 3, 4 or 5 alone (no roofline or CPU
+    baseline objects: those belong to the default line)."""
+    from segment_autoregressive_dit_amd import nomas, synth
+    import torch
+    line = {"metric": "segment-attention TFLOP/s + % MFMA peak; ms per denoise step (54 blocks)", "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if args.config == 1:
+        wl = synth.WORKLOADS["tiny"]
+        cache = nomas.KVCache(wl.n_heads, wl.head_dim, wl.tpf, wl.capacity_frames, False)
+        kb, vb = synth.prefill_kv(wl)
+        cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+        q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+        out = torch.empty_like(q)
+        ms = time_launches(lambda: nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out),
+                           args.steps)
+        value, ms_step = wl.attention_flop() / ms / 1e9, ms
+        line["config"] = {"workload": "tiny: 2x64 heads, 4x6 grid, 4 cached frames, 2-frame segment + 16 text "
+                                      "(a correctness shape; its time is launch-bound)"}
+        extra = {"attention_ms": round(ms, 5)}
+    elif args.config == 3:
+        extra = layer_int8_bench(reps=args.steps)
+        value, ms_step = extra["int8_attention_tflops"], extra["int8_attention_ms"]
+        line["config"] = {"workload": "single layer, INT8 window: 16x128 heads, 24x40 grid, 18 frames, 8-frame "
+                                      "segment + 256 text; 4 outlier key channels per head at 20x"}
+    elif args.config == 4:
+        extra = long_history_bench(reps=args.steps)
+        value, ms_step = extra["long_history_tflops"], extra["long_history_ms"]["auto"]
+        line["config"] = {"workload": "full history, bf16: 84,480 cached tokens (88 frames) + 7,936 queries, "
+                                      "16x128 heads, automatic split-KV"}
+    else:
+        d = denoise_bench()
+        value, ms_step = d["denoise_tflops"], d["denoise_ms_per_step"]
+        extra = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+        line["config"] = {"workload": "denoise sweep: 54 layers x 8 steps x 3 turns of RoPE + attention against "
+                                      "INT8 18-frame windows, 54 appends per turn; ms_per_step = median step"}
+    line.update(value=round(value, 2), ms_per_step=round(ms_step, 4), extra=extra)
+    line["config"]["parallelism"] = "single GPU"
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -674,6 +740,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     from segment_autoregressive_dit_amd import nomas
     nomas.lib()
+    if args.config != 2:
+        single_config(args)
+        return
 
     wl, r = layer_step_bench(args)
     value = r["flop"] / (r["ms_per_step"] * 1e-3) / 1e12

@@ -87,3 +87,52 @@ def test_restore_rebuilds_the_cache(int8):
     for x, y in zip(cache_slots(a), cache_slots(b)):
         if x is not None:
             assert np.array_equal(x[:n], y[:n])
+
+
+def _session_step(cache, s, H, D, gh, gw, F, T):
+    """Segment s of a seeded session: RoPE of its Q/K video rows, attention
+    against the cache, then the append of its K/V; returns the attention output."""
+    tpf = gh * gw
+    nv, n = F * tpf, F * tpf + T
+    q, k, v = (dev_bf16(synth.normal_bf16((n, H, D), 92, s, 0, t)) for t in range(3))
+    nomas.nomas_rope3d(q, k, F * s, F, gh, gw, (D // 4, 3 * D // 8, 3 * D // 8), H, D)
+    out = nomas.nomas_segment_attention(q, k, v, nv, T, cache)
+    cache.nomas_kvcache_append(k[:nv], v[:nv], F)
+    return out
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_resume_from_archive_is_bitwise_the_uninterrupted_session(int8):
+    """Checkpoint / resume: after segment 2 of a 6-segment session the retained
+    frames go to pinned host memory as records and the cache is dropped; a fresh
+    cache whose frames_written is set to the snapshot's count minus the retained
+    frames takes the records back (each lands in its original slot) and the
+    session continues. Every later attention output and the final cache bytes
+    equal the uninterrupted session's bit for bit."""
+    H, D, gh, gw, F, T, W = 2, 128, 4, 10, 2, 24, 5
+    tpf = gh * gw
+    ref = nomas.KVCache(H, D, tpf, W, int8)
+    outs_ref = [_session_step(ref, s, H, D, gh, gw, F, T) for s in range(6)]
+    torch.cuda.synchronize()
+    say(f"resume: int8={int8}")
+    a = nomas.KVCache(H, D, tpf, W, int8)
+    for s in range(3):
+        _session_step(a, s, H, D, gh, gw, F, T)
+    fw, valid = a.frames_written, a.valid_frames
+    host = a.host_records(valid)
+    a.nomas_kvcache_export_frames(fw - valid, valid, host)
+    torch.cuda.synchronize()
+    del a
+    b = nomas.KVCache(H, D, tpf, W, int8)
+    b.desc.frames_written = fw - valid
+    b.nomas_kvcache_restore_frames(host, valid)
+    assert b.frames_written == fw
+    outs = [_session_step(b, s, H, D, gh, gw, F, T) for s in range(3, 6)]
+    torch.cuda.synchronize()
+    for s, o in zip(range(3, 6), outs):
+        assert torch.equal(o, outs_ref[s]), f"segment {s} after the resume differs"
+    assert b.frames_written == ref.frames_written
+    n = b.valid_frames * tpf
+    for x, y in zip(cache_slots(b), cache_slots(ref)):
+        if x is not None:
+            assert np.array_equal(x[:n], y[:n])

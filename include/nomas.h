@@ -93,6 +93,15 @@ typedef struct nomas_kvcache {
 /* Library version, (major << 16) | minor. */
 int32_t nomas_version(void);
 
+/* Checking build only (libnomas_debug.so, compiled with NOMAS_DEVICE_CHECKS):
+ * the kernels test every cache slot, token range and tile row they address
+ * against the buffer it must stay in, count each failed test on the device and
+ * skip that access. Returns the count since the last reset on the current
+ * device (reset != 0 clears it; the call synchronises with the device), or -1
+ * in the normal build, whose kernels carry no checks. For debugging and test
+ * harnesses. */
+int64_t nomas_device_check_failures(int32_t reset);
+
 /* Text of the last error on the calling thread ("" if none). Valid until the
  * next call into the library on that thread. */
 const char* nomas_last_error(void);

@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnomas.so")
+DEBUG_LIB = os.path.join(HERE, "libnomas_debug.so")   # the checking build (NOMAS_DEVICE_CHECKS)
 SOURCES = ["nomas_host.cpp", "rope3d.hip", "kvcache_append.hip", "kvcache_archive.cpp", "attention.hip",
            "sparse_select.hip", "qkv_gemm.hip"]
 
@@ -39,11 +40,14 @@ ASAN_RUNTIME = os.path.join(os.path.dirname(HIPCC), "..", "lib", "llvm", "lib", 
                             "libclang_rt.asan-x86_64.so")
 
 
-def build(verbose=True, jobs=4, sanitize=False, out=None):
+def build(verbose=True, jobs=4, sanitize=False, out=None, checks=False):
     """Compile every source for gfx950 and link ``out`` (default: libnomas.so
-    next to this file). ``sanitize``: host code with ASan + UBSan."""
-    lib = out or LIB
-    extra = SANITIZE_FLAGS if sanitize else []
+    next to this file, or libnomas_debug.so with ``checks``). ``sanitize``: host
+    code with ASan + UBSan. ``checks``: the kernels test every cache slot, token
+    range and tile row they address (NOMAS_DEVICE_CHECKS; see
+    nomas_device_check_failures)."""
+    lib = out or (DEBUG_LIB if checks else LIB)
+    extra = (SANITIZE_FLAGS if sanitize else []) + (["-DNOMAS_DEVICE_CHECKS"] if checks else [])
     with tempfile.TemporaryDirectory(prefix="nomas_build_") as tmp:
         objs, procs = [], []
         for src in SOURCES:

@@ -347,13 +347,11 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
   auto tile_rows = [&](int t, auto cache_tag, int& key0, int& nvalid, int& klo) {
     constexpr bool CACHE = decltype(cache_tag)::value;
     klo = 0;
+    // (the list entry is the same for the whole block: keep it scalar)
     if constexpr (MS) {
       key0 = kbase + t * BC;
       nvalid = min(BC, kend - key0);
-      return;
-    }
-    // (the list entry is the same for the whole block: keep it scalar)
-    if constexpr (SP && CACHE) {
+    } else if constexpr (SP && CACHE) {
       key0 = __builtin_amdgcn_readfirstlane(blist[t / TPB]) * kSpKeyBlock + (t % TPB) * BC;
       nvalid = min(BC, a.n_cached - key0);
     } else if constexpr (CACHE) {
@@ -374,6 +372,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       key0 = __builtin_amdgcn_readfirstlane((t - tiles_c_b) * BC);
       nvalid = min(BC, a.n_cur - key0);
     }
+#ifdef NOMAS_DEVICE_CHECKS
+    // checking build: a tile that would read outside its buffer reads rows
+    // [0, BC) instead, all masked
+    const bool fits = CACHE ? key0 >= 0 && key0 + BC <= a.pitch_c && klo >= 0 && klo + nvalid <= BC
+                            : key0 >= 0 && key0 + nvalid <= a.n_cur && key0 + BC <= a.pitch_cur;
+    if (!NOMAS_IN_BOUNDS(fits)) key0 = 0, nvalid = 0, klo = 0;
+#endif
   };
   auto tile_info = [&](int t, auto cache_tag, int& key0, int& nvalid) {
     int klo;
@@ -1313,6 +1318,7 @@ extern "C" int32_t nomas_segment_attention_sparse(const uint16_t* q, const uint1
 // returns for the current device, looked up on the entry point's first call
 // there and kept per device.
 namespace nomas {
+int64_t check_failures_attention(int reset) { return source_check_failures(reset); }
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
@@ -1406,7 +1412,10 @@ static int32_t make_seg_plan(const nomas_segment* segs, int32_t n_segments, int3
   p.t.qtile0[n_segments] = (int)tiles;
   p.n_rows = (int)rows;
   p.n_qtiles = (int)tiles;
-  p.pitch = (int)round_up(rows, kTokenAlign);
+  // V^T pitch: a range's partial tail tile starts anywhere (segments are not
+  // tile-aligned) and reads a whole tile of columns, so one more 128-column
+  // block of (zero) padding keeps every tile's columns inside the buffer
+  p.pitch = (int)round_up(rows, kTokenAlign) + kTokenAlign;
   p.bytes = round_up((int64_t)H * D * p.pitch * 2, 256);
   return NOMAS_OK;
 }

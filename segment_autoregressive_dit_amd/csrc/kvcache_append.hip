@@ -39,6 +39,11 @@ struct AppendArgs {
   float* vs;
 };
 
+// slot tokens [s, s + n) lie inside the ring's capacity * tpf rows (NOMAS_IN_BOUNDS)
+__device__ __forceinline__ bool slots_in_ring(const AppendArgs& a, int s, int n) {
+  return s >= 0 && s + n <= a.cap * a.tpf && blockIdx.y < (unsigned)a.n_heads;
+}
+
 __device__ __forceinline__ int slot_token(const AppendArgs& a, int r) {
   const int fi = r / a.tpf;
   int slot = a.base_slot + fi;
@@ -132,7 +137,10 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
     const float sc = m / 127.0f;
     const float rc = code_recip(sc);
     sr[kv][t] = make_float2(sc, rc);
-    if (tok0 + t < a.rows) (kv ? a.vs : a.ks)[(int64_t)h * a.pitch + slot_token(a, tok0 + t)] = sc;
+    if (tok0 + t < a.rows) {
+      const int st = slot_token(a, tok0 + t);
+      if (NOMAS_IN_BOUNDS(slots_in_ring(a, st, 1))) (kv ? a.vs : a.ks)[(int64_t)h * a.pitch + st] = sc;
+    }
   }
   __syncthreads();
   if (r0 >= a.rows) return;
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
     const float2 q = sr[0][8 * tg + i];
     float f[8];
     codes8(kx[i], q.x, q.y, f);
-    if (VEC8 || slot[i] >= 0)
+    if ((VEC8 || slot[i] >= 0) && NOMAS_IN_BOUNDS(slots_in_ring(a, slot[i], 1)))
       *reinterpret_cast<uint2*>(kc + (int64_t)slot[i] * D) = make_uint2(pack4(f[0], f[1], f[2], f[3]),
                                                                        pack4(f[4], f[5], f[6], f[7]));
   }
@@ -168,6 +176,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
   }
   int8_t* vc = static_cast<int8_t*>(a.vc) + ((int64_t)h * D + c0) * a.pitch;
   if constexpr (VEC8) {
+    if (!NOMAS_IN_BOUNDS(slots_in_ring(a, slot[0], 8))) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       *reinterpret_cast<uint2*>(vc + (int64_t)e * a.pitch + slot[0]) =
@@ -176,6 +185,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (slot[i] < 0) break;
+      if (!NOMAS_IN_BOUNDS(slots_in_ring(a, slot[i], 1))) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         vc[(int64_t)e * a.pitch + slot[i]] = static_cast<int8_t>(__float_as_uint(fv[i][e]) & 0xffu);
@@ -208,6 +218,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_bf16_kernel(AppendArgs a) {
   uint16_t* vc = static_cast<uint16_t*>(a.vc);
   if constexpr (VEC8) {   // rows is a multiple of tpf, so all 8 rows are live
     const int s0 = slot_token(a, r0);
+    if (!NOMAS_IN_BOUNDS(slots_in_ring(a, s0, 8))) return;
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(kc + ((int64_t)h * a.pitch + s0 + i) * D + d0) = kx[i];
 #pragma unroll
@@ -225,6 +236,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_bf16_kernel(AppendArgs a) {
     for (int i = 0; i < 8; ++i) {
       if (r0 + i >= a.rows) break;
       const int st = slot_token(a, r0 + i);
+      if (!NOMAS_IN_BOUNDS(slots_in_ring(a, st, 1))) continue;
       *reinterpret_cast<u32x4*>(kc + ((int64_t)h * a.pitch + st) * D + d0) = kx[i];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -268,6 +280,10 @@ int32_t validate_cache(const nomas_kvcache* c, const char* who) {
   return NOMAS_OK;
 }
 
+}  // namespace nomas
+
+namespace nomas {
+int64_t check_failures_append(int reset) { return source_check_failures(reset); }
 }  // namespace nomas
 
 using namespace nomas;

@@ -21,6 +21,35 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // Token rows reserved per head in a cache buffer (multiple of the largest key tile).
 constexpr int kTokenAlign = 128;
 
+// ---- device-side index checks. In a build with NOMAS_DEVICE_CHECKS defined,
+// NOMAS_IN_BOUNDS(c) evaluates c, counts each false one in the source file's
+// failure counter and returns it, so the access it guards is skipped instead
+// of leaving its buffer; otherwise it is the constant true and c is not even
+// evaluated (the kernels compile as if the guard were absent).
+#ifdef NOMAS_DEVICE_CHECKS
+static __device__ unsigned int g_check_failures;
+__device__ __forceinline__ bool in_bounds_counted(bool c) {
+  if (!c) atomicAdd(&g_check_failures, 1u);
+  return c;
+}
+#define NOMAS_IN_BOUNDS(c) (::nomas::in_bounds_counted(c))
+// this source file's failure count (reset: also clear it); needs the device current
+static inline int64_t source_check_failures(int reset) {
+  unsigned int v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_failures), sizeof v, 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return -1;
+  if (reset) {
+    const unsigned int z = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_failures), &z, sizeof z, 0, hipMemcpyHostToDevice) != hipSuccess)
+      return -1;
+  }
+  return v;
+}
+#else
+#define NOMAS_IN_BOUNDS(c) true
+static inline int64_t source_check_failures(int) { return -1; }
+#endif
+
 // ---- device helpers ----
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;

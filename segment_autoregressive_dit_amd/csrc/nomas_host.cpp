@@ -30,6 +30,11 @@ int32_t check_launch(const char* what) {
   return ok();
 }
 
+// failure counters of the checking build, one per source file with checks
+int64_t check_failures_append(int reset);
+int64_t check_failures_qkv(int reset);
+int64_t check_failures_attention(int reset);
+
 }  // namespace nomas
 
 using namespace nomas;
@@ -37,6 +42,16 @@ using namespace nomas;
 extern "C" {
 
 int32_t nomas_version(void) { return (0 << 16) | 1; }
+
+int64_t nomas_device_check_failures(int32_t reset) {
+  const int64_t parts[3] = {check_failures_append(reset), check_failures_qkv(reset), check_failures_attention(reset)};
+  int64_t total = 0;
+  for (int64_t p : parts) {
+    if (p < 0) return -1;
+    total += p;
+  }
+  return total;
+}
 
 const char* nomas_last_error(void) { return g_err; }
 

@@ -187,6 +187,7 @@ __device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][
       const int r = t0 + 16 * chunk;
       uint16_t* dst = vt + (int64_t)cl * a.ld_vt + r;
       const uint16_t* src = reinterpret_cast<const uint16_t*>(st) + cl * WN + 16 * chunk;
+      if (!NOMAS_IN_BOUNDS(hc + cl < a.hd && r >= 0 && a.n_rows <= a.ld_vt)) continue;
       if (r + 16 <= a.n_rows) {
         reinterpret_cast<u32x4*>(dst)[0] = reinterpret_cast<const u32x4*>(src)[0];
         reinterpret_cast<u32x4*>(dst)[1] = reinterpret_cast<const u32x4*>(src)[1];
@@ -207,7 +208,10 @@ __device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int r = t0 + 16 * j + i16;
-        if (r >= a.app_row0 && r < a.n_video) sdst[gemm_slot_token(a, r)] = sc[j];
+        if (r >= a.app_row0 && r < a.n_video) {
+          const int st = gemm_slot_token(a, r);
+          if (NOMAS_IN_BOUNDS(st >= 0 && st < a.cap * a.tpf)) sdst[st] = sc[j];
+        }
       }
     }
   }
@@ -233,7 +237,9 @@ __device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][
     for (int j = 0; j < TJ; ++j) {
       const int r = t0 + 16 * j + i16;
       if (r < a.app_row0 || r >= a.n_video) continue;
-      unsigned char* row = static_cast<unsigned char*>(cache) + ((int64_t)h * a.pitch + gemm_slot_token(a, r)) * D * ES;
+      const int stk = gemm_slot_token(a, r);
+      if (!NOMAS_IN_BOUNDS(stk >= 0 && stk < a.cap * a.tpf && cin0 + WM <= D)) continue;
+      unsigned char* row = static_cast<unsigned char*>(cache) + ((int64_t)h * a.pitch + stk) * D * ES;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         float f[4];
@@ -269,7 +275,9 @@ __device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][
       const int cl = (k * 64 + lane) / CH, chunk = (k * 64 + lane) % CH;
       const int r = t0 + 16 * chunk;
       if (r < a.app_row0 || r >= a.n_video) continue;
-      unsigned char* dst = vt + ((int64_t)cl * a.pitch + gemm_slot_token(a, r)) * ES;
+      const int sv = gemm_slot_token(a, r);
+      if (!NOMAS_IN_BOUNDS(sv >= 0 && sv + 16 <= a.cap * a.tpf)) continue;
+      unsigned char* dst = vt + ((int64_t)cl * a.pitch + sv) * ES;
       const unsigned char* src = st + (cl * WN + 16 * chunk) * ES;
 #pragma unroll
       for (int b = 0; b < ES; ++b)
@@ -279,7 +287,9 @@ __device__ __forceinline__ void kv_epilogue(const GemmArgs& a, f32x4 (&acc)[TI][
     for (int k = lane; k < WM * WN; k += 64) {
       const int cl = k / WN, tl = k % WN, r = t0 + tl;
       if (r < a.app_row0 || r >= a.n_video) continue;
-      unsigned char* dst = vt + ((int64_t)cl * a.pitch + gemm_slot_token(a, r)) * ES;
+      const int sv = gemm_slot_token(a, r);
+      if (!NOMAS_IN_BOUNDS(sv >= 0 && sv < a.cap * a.tpf)) continue;
+      unsigned char* dst = vt + ((int64_t)cl * a.pitch + sv) * ES;
       const unsigned char* src = st + (cl * WN + tl) * ES;
 #pragma unroll
       for (int b = 0; b < ES; ++b) dst[b] = src[b];
@@ -516,6 +526,7 @@ extern "C" int32_t nomas_rope3d_table(float* table, int32_t head_dim, int32_t t0
 
 namespace nomas {
 int32_t validate_cache(const nomas_kvcache* c, const char* who);
+int64_t check_failures_qkv(int reset) { return source_check_failures(reset); }
 
 static int32_t qkv_projection_impl(const char* who, const uint16_t* x, int64_t ld_x, int32_t n_rows, int32_t hidden,
                                    const uint16_t* w, int64_t ld_w, int32_t n_heads, int32_t head_dim,

@@ -65,6 +65,7 @@ def lib():
     seg_p = ctypes.POINTER(Segment)
     sig = {
         "nomas_version": (i32, []),
+        "nomas_device_check_failures": (i64, [i32]),
         "nomas_last_error": (ctypes.c_char_p, []),
         "nomas_kvcache_token_pitch": (i64, [i32, i32]),
         "nomas_kvcache_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
@@ -147,6 +148,12 @@ def _host_buffer(t, nbytes, name):
 
 def nomas_version():
     return lib().nomas_version()
+
+
+def nomas_device_check_failures(reset=False):
+    """Failed device-side index checks since the last reset (the checking
+    build, libnomas_debug.so), or -1 for the normal build."""
+    return lib().nomas_device_check_failures(int(bool(reset)))
 
 
 def nomas_kvcache_bytes(n_heads, head_dim, tokens_per_frame, capacity_frames, kv_dtype, which):

@@ -210,7 +210,9 @@ def test_block_causal_rejects_before_launch():
     L = nomas.lib()
     segs = nomas._segments([(48, 16, 0), (48, 16, 2)])
     need = L.nomas_block_causal_attention_workspace_bytes(segs, 2, 24, 2, 64)
-    assert need == 2 * 64 * 128 * 2          # V^T of 128 rows (one 128-row pitch)
+    # V^T of 128 rows: a 128-row pitch plus one 128-column block of padding (a
+    # segment's partial tail tile reads a whole tile of columns)
+    assert need == 2 * 64 * 256 * 2
     p = ctypes.c_void_p(1 << 24)
     ws = ctypes.c_void_p(1 << 26)
 

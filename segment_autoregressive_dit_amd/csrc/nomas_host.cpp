@@ -34,6 +34,8 @@ int32_t check_launch(const char* what) {
 int64_t check_failures_append(int reset);
 int64_t check_failures_qkv(int reset);
 int64_t check_failures_attention(int reset);
+int64_t check_failures_sparse(int reset);
+int64_t check_failures_rope(int reset);
 
 }  // namespace nomas
 
@@ -44,7 +46,8 @@ extern "C" {
 int32_t nomas_version(void) { return (0 << 16) | 1; }
 
 int64_t nomas_device_check_failures(int32_t reset) {
-  const int64_t parts[3] = {check_failures_append(reset), check_failures_qkv(reset), check_failures_attention(reset)};
+  const int64_t parts[5] = {check_failures_append(reset), check_failures_qkv(reset), check_failures_attention(reset),
+                            check_failures_sparse(reset), check_failures_rope(reset)};
   int64_t total = 0;
   for (int64_t p : parts) {
     if (p < 0) return -1;

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(uint16_t* __restri
     const int row = row0 + tk;
     if (row >= n_rows) continue;
     const int h = c / CPR, d0 = (c - h * CPR) * 8;
+    if (!NOMAS_IN_BOUNDS(h < n_heads && d0 + 8 <= D && (int64_t)n_heads * D <= ld)) continue;
     uint16_t* base = tensor ? k : q;
     u32x4* ptr = reinterpret_cast<u32x4*>(base + (int64_t)row * ld + (int64_t)h * D + d0);
     u32x4 v = *ptr;
@@ -67,6 +68,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope3d_kernel(uint16_t* __restri
     *ptr = o;
   }
 }
+
+int64_t check_failures_rope(int reset) { return source_check_failures(reset); }
 
 }  // namespace nomas
 

@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void sp_mean_k_kernel(const void* __restrict__
 #pragma unroll 4
   for (int r = r0 + g; r < r1; r += RG) {
     const int64_t row = (int64_t)h * pitch + r;
+    if (!NOMAS_IN_BOUNDS(r < pitch)) break;
     if constexpr (I8) {
       const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(kc) + row * D + c0);
       const float sc = ks[row];
@@ -104,6 +105,7 @@ __global__ __launch_bounds__(256) void sp_select_kernel(const float* __restrict_
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   if (tid < D) qv[tid] = mq[((int64_t)h * nqb + b) * D + tid];
   __syncthreads();
+  if (!NOMAS_IN_BOUNDS(nc <= kSpMaxCandidates)) return;
   for (int c = tid; c < nc; c += 256) {
     const float* kr = mk + ((int64_t)h * nc + c) * D;
     float s = 0.f;
@@ -128,6 +130,8 @@ __global__ __launch_bounds__(256) void sp_select_kernel(const float* __restrict_
 
   }
 }
+
+int64_t check_failures_sparse(int reset) { return source_check_failures(reset); }
 
 }  // namespace nomas
 

@@ -1,5 +1,5 @@
-"""The GPU parity tests of the cache, frame-range, fused-projection, block-causal
-and sparse paths run against the checking build (libnomas_debug.so: every
+"""The GPU parity tests of the RoPE, cache, frame-range, fused-projection,
+block-causal and sparse paths run against the checking build (libnomas_debug.so: every
 cache slot, token range and tile row a kernel addresses is tested against its
 buffer, failures counted on the device and the access skipped). They must pass
 as they do on the normal build, with no failed check.
@@ -39,7 +39,8 @@ sys.exit(int(rc) if rc else (0 if n == 0 else 3))
 def test_parity_tests_pass_on_the_checking_build_with_no_failed_check():
     assert os.path.exists(B.DEBUG_LIB), "libnomas_debug.so is missing (build() builds it)"
     t = os.path.join(ROOT, "tests")
-    args = [os.path.join(t, "test_gpu_kvcache.py"), os.path.join(t, "test_gpu_frames.py"),
+    args = [os.path.join(t, "test_gpu_rope.py"), os.path.join(t, "test_gpu_kvcache.py"),
+            os.path.join(t, "test_gpu_frames.py"),
             os.path.join(t, "test_gpu_pipeline.py"), os.path.join(t, "test_gpu_block_causal.py"),
             os.path.join(t, "test_gpu_sparse.py"),
             os.path.join(t, "test_gpu_qkv.py") + "::test_projection_append_equals_projection_then_append",

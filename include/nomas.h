@@ -59,8 +59,12 @@ typedef enum { NOMAS_KV_BF16 = 0, NOMAS_KV_INT8 = 1 } nomas_kv_dtype;
 /*
  * Ring-buffer KV cache of one layer: a window of `capacity_frames` latent
  * frames of `tokens_per_frame` video tokens each. Caller-owned plain data;
- * fill it with nomas_kvcache_init. Only nomas_kvcache_append changes it
- * (frames_written).
+ * fill it with nomas_kvcache_init. The library changes only frames_written,
+ * in the calls that append frames (nomas_kvcache_append, ..._append_archive,
+ * ..._restore_frames, nomas_qkv_projection_append). A caller may set
+ * frames_written itself, e.g. to resume a session from archived records: with
+ * frames_written = F - n, restoring the records of frames F - n .. F - 1 puts
+ * each back in its original slot.
  *
  * Frame f of the session (f = 0, 1, ... in append order) is stored in slot
  * f mod capacity_frames while it is retained; the retained frames are the last

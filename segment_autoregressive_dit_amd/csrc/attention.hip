@@ -521,6 +521,13 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         *reinterpret_cast<u32x4*>(Ks + row * D * 2 + (((2 * cc + 1) ^ s) * 16)) = hi;
         __builtin_amdgcn_sched_barrier(0);   // one piece at a time: few live registers
       }
+      // the key scales wave 0 copied (its copies have landed) become the
+      // exponent coefficients scale * c2, once per tile for the whole block
+      if (wave == 0) {
+        float* ksc = reinterpret_cast<float*>(Ks + C::KT_BYTES);
+#pragma unroll
+        for (int j = 0; j < BC / 64; ++j) ksc[j * 64 + lane] *= a.c2;
+      }
     }
   };
   // INT8: the value scales of the lane's 16 keys (keys 16*cc .. 16*cc+15)
@@ -612,12 +619,9 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (SCALED) {
-      const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES);
+      const float* sc = reinterpret_cast<const float*>(kbuf(i) + C::KT_BYTES);   // scale * c2 per key
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const f32x4 ksv = *reinterpret_cast<const f32x4*>(sc + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1));
-        kcs[kb] = ksv * a.c2;
-      }
+      for (int kb = 0; kb < NKB; ++kb) kcs[kb] = *reinterpret_cast<const f32x4*>(sc + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1));
     }
   };
 

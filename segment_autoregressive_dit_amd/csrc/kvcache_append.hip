@@ -14,7 +14,7 @@
 // An append of n frames writes only its last min(n, capacity) frames, so no two
 // tokens of one launch target the same slot and the launch is race-free.
 //
-// INT8 kernel (kv_append_i8_kernel): one block = 128 tokens of one head; codes
+// INT8 kernel (kv_append_i8_kernel): one wave = a run of tokens of one head; codes
 // from a reciprocal product with an exact test that sends the rare codes near a
 // rounding boundary to the IEEE quotient; V transposed in registers. The BF16
 // cache has a copy kernel of its own (kv_append_bf16_kernel). Both are described
@@ -68,6 +68,15 @@ __device__ __forceinline__ float absmax8(const u32x4 w) {
   return __uint_as_float(mx << 16);
 }
 
+// orders a wave's LDS writes before its later LDS reads of other lanes' data:
+// the compiler may not move memory operations across the fences, and the LDS
+// executes one wave's operations in issue order
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // the 8 codes (as C + code floats, see code_fast / code_exact in
 // nomas_common.hpp) of one token's 16-byte chunk
 __device__ __forceinline__ bool codes8(const u32x4 w, float s, float r, float (&f)[8]) {
@@ -81,27 +90,32 @@ __device__ __forceinline__ bool codes8(const u32x4 w, float s, float r, float (&
   return ok;
 }
 
-// One block = 128 tokens x D channels of one head, D/32 waves; wave w owns
-// channels [32w, 32w+32). Lane = tg + 16*cc: tokens 8tg..8tg+7 of the block,
-// channels 32w + 8cc .. +8, so a lane loads 8 rows x 16 bytes of K and of V.
-// A token's absmax: over the lane's chunk, then over the wave's 4 chunk lanes
-// (two row swaps, which leave the K maxima in rows 0 and 2 and the V maxima in
-// rows 1 and 3), then across waves through LDS; one thread per (token, K or V)
-// then forms the scale and its reciprocal. K codes go out as 8-byte row pieces;
-// V codes are transposed in registers (8 tokens x 8 channels), so 16 lanes
-// store a 128-byte run of one channel's tokens. VEC8 (tokens per frame a
-// multiple of 8): a lane's 8 tokens sit in 8 consecutive slots; otherwise V^T
-// goes out byte by byte.
+// One wave = TW tokens x D channels of one head (D = 128: 32 tokens, D = 64:
+// 64), four independent waves per block. Lane = cc + CL*tg: channels
+// 8cc..8cc+7 of the run's tokens 8tg..8tg+7, so a lane loads 8 rows x 16 bytes
+// of K and of V and each load instruction covers TG whole rows. A token's
+// absmax forms inside the wave: the lanes put their chunk maxima into the
+// wave's own LDS region, one lane per (K or V, token) reduces the CL chunk
+// maxima of its token and forms the scale and its reciprocal, and every lane
+// reads back those of its 8 tokens. A wave only reads what it wrote itself, so
+// no block barrier holds one wave for another. K codes go out as 8-byte row
+// pieces (the CL lanes of a token store its D bytes); V codes are transposed
+// in registers (8 tokens x 8 channels), so the TG lanes of a channel store a
+// TW-byte run of its slots, and the four waves of a block the adjacent runs.
+// VEC8 (tokens per frame a multiple of 8): a lane's 8 tokens sit in 8
+// consecutive slots; otherwise V^T goes out byte by byte.
 template <int D, bool VEC8>
-__global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
-  constexpr int NW = D / 32, NT = 2 * D, TOK = 128;
-  __shared__ __align__(16) float red[NW][2][TOK];    // per-wave absmax of each token (K, V)
-  __shared__ __align__(16) float2 sr[2][TOK];         // (scale, reciprocal) of each token (K, V)
-  const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tg = lane & 15, cc = lane >> 4;
-  const int tok0 = blockIdx.x * TOK;
-  const int r0 = tok0 + 8 * tg;                    // the lane's first row
-  const int c0 = 32 * wave + 8 * cc;               // and first channel
+__global__ __launch_bounds__(256) void kv_append_i8_kernel(AppendArgs a) {
+  constexpr int CL = D / 8, TG = 64 / CL, TW = 8 * TG, NV = 2 * TW;   // NV: (K or V, token) pairs
+  constexpr int RP = NV + 4;                          // padded row: chunk rows start 16 B apart in the banks
+  __shared__ __align__(16) float red[4][CL * RP];     // per wave: chunk maxima [chunk][kv * TW + token]
+  __shared__ __align__(16) float2 sr[4][NV];          // per wave: (scale, reciprocal) [kv * TW + token]
+  const int h = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cc = lane % CL, tg = lane / CL;
+  const int tok0 = (blockIdx.x * 4 + wave) * TW;
+  if (tok0 >= a.rows) return;                        // the whole wave
+  const int r0 = tok0 + 8 * tg;                      // the lane's first row
+  const int c0 = 8 * cc;                             // and first channel
 
   u32x4 kx[8], vx[8];
 #pragma unroll
@@ -110,39 +124,29 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
     kx[i] = *reinterpret_cast<const u32x4*>(a.k_new + src);
     vx[i] = *reinterpret_cast<const u32x4*>(a.v_new + src);
   }
+  __builtin_amdgcn_sched_barrier(0);   // all 16 loads in flight before the first wait
 
-  // ---- absmax of each token
-  float mx[8];
+  // ---- absmax of each token: chunk maxima -> LDS -> one lane per (K or V, token)
+  float* rw = &red[wave][cc * RP + 8 * tg];
+  *reinterpret_cast<f32x4*>(rw) = (f32x4){absmax8(kx[0]), absmax8(kx[1]), absmax8(kx[2]), absmax8(kx[3])};
+  *reinterpret_cast<f32x4*>(rw + 4) = (f32x4){absmax8(kx[4]), absmax8(kx[5]), absmax8(kx[6]), absmax8(kx[7])};
+  *reinterpret_cast<f32x4*>(rw + TW) = (f32x4){absmax8(vx[0]), absmax8(vx[1]), absmax8(vx[2]), absmax8(vx[3])};
+  *reinterpret_cast<f32x4*>(rw + TW + 4) = (f32x4){absmax8(vx[4]), absmax8(vx[5]), absmax8(vx[6]), absmax8(vx[7])};
+  wave_lds_sync();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float mk = absmax8(kx[i]), mv = absmax8(vx[i]);
-    // rows 0, 2 <- max(K of rows 0|1, 2|3); rows 1, 3 <- max(V of rows 0|1, 2|3)
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(mk), __float_as_uint(mv), false, false);
-    const float m2 = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    const unsigned u2 = __float_as_uint(m2);
-    const auto q = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-    mx[i] = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-  }
-  if (cc < 2) {   // row 0 holds the K maxima, row 1 the V maxima of tokens 8tg..8tg+7
-    *reinterpret_cast<f32x4*>(&red[wave][cc][8 * tg]) = (f32x4){mx[0], mx[1], mx[2], mx[3]};
-    *reinterpret_cast<f32x4*>(&red[wave][cc][8 * tg + 4]) = (f32x4){mx[4], mx[5], mx[6], mx[7]};
-  }
-  __syncthreads();
-  // ---- scales: one (token, K or V) per thread
-  for (int p = tid; p < 2 * TOK; p += NT) {
-    const int kv = p / TOK, t = p % TOK;
-    float m = red[0][kv][t];
+  for (int p = lane; p < NV; p += 64) {
+    float m = red[wave][p];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w][kv][t]);
+    for (int j = 1; j < CL; ++j) m = fmaxf(m, red[wave][j * RP + p]);
     const float sc = m / 127.0f;
-    const float rc = code_recip(sc);
-    sr[kv][t] = make_float2(sc, rc);
-    if (tok0 + t < a.rows) {
-      const int st = slot_token(a, tok0 + t);
-      if (NOMAS_IN_BOUNDS(slots_in_ring(a, st, 1))) (kv ? a.vs : a.ks)[(int64_t)h * a.pitch + st] = sc;
+    sr[wave][p] = make_float2(sc, code_recip(sc));
+    const int t = tok0 + p % TW;
+    if (t < a.rows) {
+      const int st = slot_token(a, t);
+      if (NOMAS_IN_BOUNDS(slots_in_ring(a, st, 1))) (p >= TW ? a.vs : a.ks)[(int64_t)h * a.pitch + st] = sc;
     }
   }
-  __syncthreads();
+  wave_lds_sync();
   if (r0 >= a.rows) return;
 
   int slot[8];
@@ -156,12 +160,14 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
   }
 
   // ---- K: codes token by token, 8-byte row pieces
+  f32x4 q4[4];   // (scale, reciprocal) of the lane's 8 tokens, K then V
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q4[j] = *reinterpret_cast<const f32x4*>(&sr[wave][8 * tg + 2 * j]);
   int8_t* kc = static_cast<int8_t*>(a.kc) + (int64_t)h * a.pitch * D + c0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float2 q = sr[0][8 * tg + i];
     float f[8];
-    codes8(kx[i], q.x, q.y, f);
+    codes8(kx[i], q4[i >> 1][2 * (i & 1)], q4[i >> 1][2 * (i & 1) + 1], f);
     if ((VEC8 || slot[i] >= 0) && NOMAS_IN_BOUNDS(slots_in_ring(a, slot[i], 1)))
       *reinterpret_cast<uint2*>(kc + (int64_t)slot[i] * D) = make_uint2(pack4(f[0], f[1], f[2], f[3]),
                                                                        pack4(f[4], f[5], f[6], f[7]));
@@ -170,10 +176,9 @@ __global__ __launch_bounds__(2 * D) void kv_append_i8_kernel(AppendArgs a) {
   // ---- V: codes of 8 tokens x 8 channels, transposed to channel rows
   float fv[8][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float2 q = sr[1][8 * tg + i];
-    codes8(vx[i], q.x, q.y, fv[i]);
-  }
+  for (int j = 0; j < 4; ++j) q4[j] = *reinterpret_cast<const f32x4*>(&sr[wave][TW + 8 * tg + 2 * j]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) codes8(vx[i], q4[i >> 1][2 * (i & 1)], q4[i >> 1][2 * (i & 1) + 1], fv[i]);
   int8_t* vc = static_cast<int8_t*>(a.vc) + ((int64_t)h * D + c0) * a.pitch;
   if constexpr (VEC8) {
     if (!NOMAS_IN_BOUNDS(slots_in_ring(a, slot[0], 8))) return;
@@ -256,11 +261,12 @@ static void launch_append_bf16(const AppendArgs& a, bool vec8, hipStream_t s) {
 
 template <int D>
 static void launch_append_int8(const AppendArgs& a, bool vec8, hipStream_t s) {
-  const dim3 grid((unsigned)((a.rows + 127) / 128), (unsigned)a.n_heads);
+  constexpr int TB = 4 * 8 * (64 / (D / 8));    // tokens per block: four waves of 8 * (64 / (D/8))
+  const dim3 grid((unsigned)((a.rows + TB - 1) / TB), (unsigned)a.n_heads);
   if (vec8)
-    hipLaunchKernelGGL((kv_append_i8_kernel<D, true>), grid, dim3(2 * D), 0, s, a);
+    hipLaunchKernelGGL((kv_append_i8_kernel<D, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((kv_append_i8_kernel<D, false>), grid, dim3(2 * D), 0, s, a);
+    hipLaunchKernelGGL((kv_append_i8_kernel<D, false>), grid, dim3(256), 0, s, a);
 }
 
 int32_t validate_cache(const nomas_kvcache* c, const char* who) {

@@ -39,9 +39,10 @@ struct AppendArgs {
   float* vs;
 };
 
-// slot tokens [s, s + n) lie inside the ring's capacity * tpf rows (NOMAS_IN_BOUNDS)
-__device__ __forceinline__ bool slots_in_ring(const AppendArgs& a, int s, int n) {
-  return s >= 0 && s + n <= a.cap * a.tpf && blockIdx.y < (unsigned)a.n_heads;
+// head h exists and slot tokens [s, s + n) lie inside the ring's capacity * tpf
+// rows (NOMAS_IN_BOUNDS)
+__device__ __forceinline__ bool slots_in_ring(const AppendArgs& a, int h, int s, int n) {
+  return h >= 0 && h < a.n_heads && s >= 0 && s + n <= a.cap * a.tpf;
 }
 
 __device__ __forceinline__ int slot_token(const AppendArgs& a, int r) {
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void kv_append_i8_kernel(AppendArgs a) {
     const int t = tok0 + p % TW;
     if (t < a.rows) {
       const int st = slot_token(a, t);
-      if (NOMAS_IN_BOUNDS(slots_in_ring(a, st, 1))) (p >= TW ? a.vs : a.ks)[(int64_t)h * a.pitch + st] = sc;
+      if (NOMAS_IN_BOUNDS(slots_in_ring(a, h, st, 1))) (p >= TW ? a.vs : a.ks)[(int64_t)h * a.pitch + st] = sc;
     }
   }
   wave_lds_sync();
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void kv_append_i8_kernel(AppendArgs a) {
   for (int i = 0; i < 8; ++i) {
     float f[8];
     codes8(kx[i], q4[i >> 1][2 * (i & 1)], q4[i >> 1][2 * (i & 1) + 1], f);
-    if ((VEC8 || slot[i] >= 0) && NOMAS_IN_BOUNDS(slots_in_ring(a, slot[i], 1)))
+    if ((VEC8 || slot[i] >= 0) && NOMAS_IN_BOUNDS(slots_in_ring(a, h, slot[i], 1)))
       *reinterpret_cast<uint2*>(kc + (int64_t)slot[i] * D) = make_uint2(pack4(f[0], f[1], f[2], f[3]),
                                                                        pack4(f[4], f[5], f[6], f[7]));
   }
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void kv_append_i8_kernel(AppendArgs a) {
   for (int i = 0; i < 8; ++i) codes8(vx[i], q4[i >> 1][2 * (i & 1)], q4[i >> 1][2 * (i & 1) + 1], fv[i]);
   int8_t* vc = static_cast<int8_t*>(a.vc) + ((int64_t)h * D + c0) * a.pitch;
   if constexpr (VEC8) {
-    if (!NOMAS_IN_BOUNDS(slots_in_ring(a, slot[0], 8))) return;
+    if (!NOMAS_IN_BOUNDS(slots_in_ring(a, h, slot[0], 8))) return;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       *reinterpret_cast<uint2*>(vc + (int64_t)e * a.pitch + slot[0]) =
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256) void kv_append_i8_kernel(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (slot[i] < 0) break;
-      if (!NOMAS_IN_BOUNDS(slots_in_ring(a, slot[i], 1))) continue;
+      if (!NOMAS_IN_BOUNDS(slots_in_ring(a, h, slot[i], 1))) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         vc[(int64_t)e * a.pitch + slot[i]] = static_cast<int8_t>(__float_as_uint(fv[i][e]) & 0xffu);
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_bf16_kernel(AppendArgs a) {
   uint16_t* vc = static_cast<uint16_t*>(a.vc);
   if constexpr (VEC8) {   // rows is a multiple of tpf, so all 8 rows are live
     const int s0 = slot_token(a, r0);
-    if (!NOMAS_IN_BOUNDS(slots_in_ring(a, s0, 8))) return;
+    if (!NOMAS_IN_BOUNDS(slots_in_ring(a, h, s0, 8))) return;
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(kc + ((int64_t)h * a.pitch + s0 + i) * D + d0) = kx[i];
 #pragma unroll
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(2 * D) void kv_append_bf16_kernel(AppendArgs a) {
     for (int i = 0; i < 8; ++i) {
       if (r0 + i >= a.rows) break;
       const int st = slot_token(a, r0 + i);
-      if (!NOMAS_IN_BOUNDS(slots_in_ring(a, st, 1))) continue;
+      if (!NOMAS_IN_BOUNDS(slots_in_ring(a, h, st, 1))) continue;
       *reinterpret_cast<u32x4*>(kc + ((int64_t)h * a.pitch + st) * D + d0) = kx[i];
 #pragma unroll
       for (int j = 0; j < 8; ++j)

@@ -68,8 +68,10 @@ def build(verbose=True, jobs=4, sanitize=False, out=None, checks=False):
         if failed:
             raise RuntimeError("libnomas build failed")
         tmp_lib = lib + ".tmp"
+        # every symbol must resolve at link time: a kernel whose host stub the
+        # compiler did not emit fails here, not when the library is loaded
         link_extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
-                      "-shared-libsan"] if sanitize else []
+                      "-shared-libsan"] if sanitize else ["-Wl,-z,defs"]
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + link_extra + ["-o", tmp_lib] + objs
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:

@@ -13,16 +13,18 @@
 //    pairs (2j, 2j+1) sit in one lane and a store writes 8 contiguous bytes.
 //  * Block = 8 waves = 256 channels x 256 tokens, one block per CU; each wave
 //    owns 64 channels x 128 tokens (4 x 8 accumulator tiles). The hidden
-//    dimension is walked in steps of 32: both 256 x 32 operand tiles are copied
-//    global -> LDS by the load unit (buffer_load ... lds) into a ring of four
-//    stages, one barrier per step, with the 16-byte chunk index XOR-swizzled by
-//    (row/4) % 4. (Block, wave tile and ring depth are the NOMAS_GEMM_CFG
-//    defaults below.)
-//  * Software pipeline: a step's MFMAs use fragments read during the previous
-//    step, while they read the next step's fragments (from a stage made
-//    resident by the previous barrier) and the load unit refills the step's own
-//    stage four steps ahead; a step waits only for the copies two steps ahead,
-//    so each copy has three steps to land.
+//    dimension is walked in steps of 64: both 256 x 64 operand tiles are copied
+//    global -> LDS by the load unit (buffer_load ... lds) into two stages, so
+//    each copy fetches whole 128-byte lines of its rows; the 16-byte chunk
+//    index is XOR-swizzled by (row/2) % 8. (Block, wave tile and ring depth are
+//    the NOMAS_GEMM_CFG defaults below.)
+//  * Software pipeline, one barrier per step: a step's first 32-deep half runs
+//    its MFMAs on fragments already in registers while the second half's
+//    fragments are read from the step's stage; after the barrier (every wave's
+//    reads of that stage done, the next step's copies landed) the load unit
+//    refills the stage with the step after next, and the second half's MFMAs
+//    run while the next step's first-half fragments are read. Each copy has a
+//    whole step to land.
 //  * Blocks are laid out so each XCD works through whole channel tiles: the
 //    W tile stays in that XCD's L2 while token tiles stream past it.
 #include <type_traits>
@@ -33,27 +35,29 @@ namespace nomas {
 
 // Block tile BM channels x BN tokens, wave tile WM x WN, ring of S stages.
 #ifndef NOMAS_GEMM_CFG
-#define NOMAS_GEMM_CFG 256, 256, 64, 128, 4, 1, 8
+#define NOMAS_GEMM_CFG 256, 256, 64, 128, 2, 1, 8
 #endif
 template <int BM_, int BN_, int WM_, int WN_, int S_, int MINB_, int GROUPN_>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_, MINB = MINB_, GROUPN = GROUPN_;
   static constexpr int NW = (BM / WM) * (BN / WN);
   static constexpr int NT = NW * 64;
-  static constexpr int BK = 32;                    // hidden elements per step
+  static constexpr int BK = 64;                    // hidden elements per step
   static constexpr int TI = WM / 16, TJ = WN / 16; // accumulator tiles per wave
   static constexpr int WBYTES = BM * BK * 2, XBYTES = BN * BK * 2;
   static constexpr int IW = WBYTES / 1024 / NW, IX = XBYTES / 1024 / NW;   // copies per wave and stage
   static constexpr int IPS = IW + IX;
   static_assert(IW * NW * 1024 == WBYTES && IX * NW * 1024 == XBYTES, "tiles must split into 1 KB copies per wave");
-  static_assert(S >= 3 && (S - 2) * IPS <= 63, "ring depth");
+  static_assert(S == 2, "two stages of 64-deep steps");
   static_assert(TJ % 2 == 0 || TI <= TJ, "fragment refill pattern");
 };
 using GC = GemmCfg<NOMAS_GEMM_CFG>;
 
-// 64-byte rows of 4 chunks; the chunk index is XOR-ed with (row / 4) % 4, so the
-// 16 rows a quarter-wave reads at one chunk fall on 16 distinct bank groups
-__device__ __forceinline__ int gemm_swz(int row) { return (row >> 2) & 3; }
+// 128-byte rows of 8 chunks; the chunk index is XOR-ed with (row / 2) % 8, so
+// the 16 rows a quarter-wave reads at one chunk fall on 16 distinct bank groups
+// (rows 2m and 2m+1 in the two halves of a 256-byte bank row, m picking the
+// chunk)
+__device__ __forceinline__ int gemm_swz(int row) { return (row >> 1) & 7; }
 
 struct GemmArgs {
   const uint16_t* x;
@@ -349,18 +353,18 @@ __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmAr
       scalar_ptr(a.x + (int64_t)tok0 * a.ld_x), (short)0,
       __builtin_amdgcn_readfirstlane((int)(max(0, min(BN, a.n_rows - tok0)) * a.ld_x * 2)), 0x00020000);
 
-  // each wave instruction fills 1 KB of LDS (16 rows of 64 B); the lane fetches
+  // each wave instruction fills 1 KB of LDS (8 rows of 128 B); the lane fetches
   // the global chunk that the swizzled layout puts at its position
   auto issue = [&](int kt, int st) {
 #pragma unroll
     for (int k = 0; k < GC::IW; ++k) {
-      const int blk = wave * GC::IW + k, row = blk * 16 + (lane >> 2), c = (lane & 3) ^ gemm_swz(row);
+      const int blk = wave * GC::IW + k, row = blk * 8 + (lane >> 3), c = (lane & 7) ^ gemm_swz(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wbuf(st) + blk * 1024),
                                                16, row * (int)a.ld_w * 2 + c * 16, kt * BK * 2, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < GC::IX; ++k) {
-      const int blk = wave * GC::IX + k, row = blk * 16 + (lane >> 2), c = (lane & 3) ^ gemm_swz(row);
+      const int blk = wave * GC::IX + k, row = blk * 8 + (lane >> 3), c = (lane & 7) ^ gemm_swz(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xbuf(st) + blk * 1024),
                                                16, row * (int)a.ld_x * 2 + c * 16, kt * BK * 2, 0, 0);
     }
@@ -372,63 +376,55 @@ __global__ __launch_bounds__(GC::NT, GC::MINB) void qkv_gemm_kernel(const GemmAr
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto read_a = [&](int st, int i) {
+  auto read_a = [&](int st, int kk, int i) {
     const int r = wch + 16 * i + i16;
-    return *reinterpret_cast<const bf16x8*>(wbuf(st) + r * 64 + ((G ^ gemm_swz(r)) * 16));
+    return *reinterpret_cast<const bf16x8*>(wbuf(st) + r * 128 + (((4 * kk + G) ^ gemm_swz(r)) * 16));
   };
-  auto read_b = [&](int st, int j) {
+  auto read_b = [&](int st, int kk, int j) {
     const int r = wtok + 16 * j + i16;
-    return *reinterpret_cast<const bf16x8*>(xbuf(st) + r * 64 + ((G ^ gemm_swz(r)) * 16));
+    return *reinterpret_cast<const bf16x8*>(xbuf(st) + r * 128 + (((4 * kk + G) ^ gemm_swz(r)) * 16));
   };
 
-  // Pipeline over a ring of S stages. Step kt computes from fragments read during
-  // step kt-1 (so stage kt%S is free) and meanwhile: the load unit fills stage
-  // kt%S with step kt+S, and the wave reads step kt+1's fragments from stage
-  // (kt+1)%S. At its end the step waits only for the copies of step kt+2 (the
-  // later ones stay in flight: S-1 steps for a copy to land), then a barrier
-  // makes them visible and retires every read of the stage refilled next.
-  // Token fragment j of the next step goes into the register of token fragment
-  // j once its MFMAs are issued; channel fragments alternate two sets.
+  // Two stages of 64-deep steps. Step kt: the first half's MFMAs (fragments in
+  // registers) while the second half's fragments are read from stage kt%2;
+  // then every wave waits for the copies of step kt+1 and for its own reads,
+  // a barrier, the copies of step kt+2 into stage kt%2 (now read out), and the
+  // second half's MFMAs while step kt+1's first-half fragments are read from
+  // stage (kt+1)%2. One barrier per step; each copy has a whole step to land.
   const int nk = a.hidden / BK;
-  for (int st = 0; st < S && st < nk; ++st) issue(st, st);
-  // wait for stages 0 and 1: the copies issued after them may stay in flight
-  if (nk >= S) wait_vm_lgkm0<(S - 2) * IPS>();
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 1) wait_vm_lgkm0<IPS>();
   else wait_vm_lgkm0<0>();
   barrier_only();
   bf16x8 fa[2][TI], fb[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) fa[0][i] = read_a(0, i);
+  for (int i = 0; i < TI; ++i) fa[0][i] = read_a(0, 0, i);
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) fb[j] = read_b(0, j);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage 0 read out before anyone refills it
-  barrier_only();
+  for (int j = 0; j < TJ; ++j) fb[j] = read_b(0, 0, j);
   // (the last step's reads of the next fragments read a stale stage and go
   // unused: cheaper than a branch per token column)
-  auto step = [&](int kt, auto cur_tag) {
+  auto half = [&](int st_next, int kk_next, auto cur_tag) {
     constexpr int C = decltype(cur_tag)::value, N = C ^ 1;
-    if (kt + S < nk) issue(kt + S, kt % S);
-    const int sn = (kt + 1) % S;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[C][i], fb[j], acc[i][j], 0, 0, 0);
-      fb[j] = read_b(sn, j);
-      // the next channel fragments, spread over the token columns
+      fb[j] = read_b(st_next, kk_next, j);
 #pragma unroll
-      for (int i = j * TI / TJ; i < (j + 1) * TI / TJ; ++i) fa[N][i] = read_a(sn, i);
+      for (int i = j * TI / TJ; i < (j + 1) * TI / TJ; ++i) fa[N][i] = read_a(st_next, kk_next, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // copies issued after step kt+2's (those of steps kt+3 .. kt+S) may stay in
-    // flight; near the end, wait for all
-    if (kt + S < nk) wait_vm_lgkm0<(S - 2) * IPS>();
-    else wait_vm_lgkm0<0>();
-    barrier_only();
   };
   using Z = std::integral_constant<int, 0>;
   using O = std::integral_constant<int, 1>;
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, Z{});
-    if (kt + 1 < nk) step(kt + 1, O{});
+  for (int kt = 0; kt < nk; ++kt) {
+    const int sc = kt & 1;
+    half(sc, 1, Z{});
+    wait_vm_lgkm0<0>();
+    barrier_only();
+    if (kt + 2 < nk) issue(kt + 2, sc);
+    half(sc ^ 1, 0, O{});
   }
 
   // ---- epilogue: RoPE on query/key channels of video rows, one bf16 rounding.

@@ -233,12 +233,24 @@ __global__ __launch_bounds__(2 * D) void kv_append_bf16_kernel(AppendArgs a) {
   const int d0 = (wave >> 1) * 64 + 8 * (lane >> 3);                     // and first channel
   if (r0 >= a.rows) return;
   u32x4 kx[8], vx[8];
+  if constexpr (VEC8) {   // rows is a multiple of 8: all 8 rows are live; one base, a scalar stride
+    const int64_t src = (int64_t)r0 * a.ld + (int64_t)h * D + d0;
+    const uint16_t* kp = a.k_new + src;
+    const uint16_t* vp = a.v_new + src;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {   // rows past the end re-read the last row and are not stored
-    const int64_t src = (int64_t)min(r0 + i, a.rows - 1) * a.ld + (int64_t)h * D + d0;
-    kx[i] = *reinterpret_cast<const u32x4*>(a.k_new + src);
-    vx[i] = *reinterpret_cast<const u32x4*>(a.v_new + src);
+    for (int i = 0; i < 8; ++i) {
+      kx[i] = *reinterpret_cast<const u32x4*>(kp + i * a.ld);
+      vx[i] = *reinterpret_cast<const u32x4*>(vp + i * a.ld);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {   // rows past the end re-read the last row and are not stored
+      const int64_t src = (int64_t)min(r0 + i, a.rows - 1) * a.ld + (int64_t)h * D + d0;
+      kx[i] = *reinterpret_cast<const u32x4*>(a.k_new + src);
+      vx[i] = *reinterpret_cast<const u32x4*>(a.v_new + src);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);   // all 16 loads in flight before the first store
   uint16_t* kc = static_cast<uint16_t*>(a.kc);
   uint16_t* vc = static_cast<uint16_t*>(a.vc);
   if constexpr (VEC8) {   // rows is a multiple of tpf, so all 8 rows are live

@@ -65,6 +65,14 @@ def test_odd_heads_key_value_boundary_inside_a_block(H):
     _run(H, 64, 128, 1, 4, 6, 9, 2, (16, 24, 24), seed=5 + H)
 
 
+@pytest.mark.parametrize("hidden", [64, 128, 192, 320])
+def test_hidden_step_counts(hidden):
+    # the hidden dimension is walked in 64-deep steps through two stages: one
+    # step (no refill at all), two (no refill inside the loop) and odd counts
+    # (the stages alternate unevenly) against the oracle
+    _run(2, 128, hidden, 1, 4, 6, 13, 5, (32, 48, 48), seed=30 + hidden)
+
+
 def test_mid_head128():
     # 4 heads of 128, hidden 512, 2 frames of 12x20 + 220 text rows
     _run(4, 128, 512, 2, 12, 20, 220, 18, (32, 48, 48), seed=1)

@@ -825,8 +825,21 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
       f32x4 sacc[QB][NKB];
       bf16x8 pf[QB][BC / 32];
       bf16x8 vf[D / 16];
-      if (grp == 1) {     // group B's idle first slot
+      // Cache tiles (codes staged through registers): group B converts its half
+      // of tile s in its H2(s-2), the slot of A's H1(s-1), and then requests
+      // tile s+1; so each slot carries one group's conversion (A's in Y, B's in
+      // X). K buffer s%2 then holds tile s-2 and V buffer s%3 tile s-3, both
+      // read by both groups in earlier slots, and the key scales stay with wave
+      // 0 (group A). Current-segment tiles, copied straight into LDS, cannot be
+      // requested three tiles ahead (the copy would land in a buffer still
+      // read): B converts them in its H1(s-1) as requested in its H2(s-2).
+      constexpr bool AHEAD = decltype(ct)::value;
+      if (grp == 1) {     // group B's first slot
         issue(1);
+        if constexpr (AHEAD) {
+          complete(1);
+          issue(2);
+        }
         __syncthreads();
       }
       for (int t = 0; t < n; ++t) {
@@ -839,13 +852,17 @@ __global__ __launch_bounds__(NW * 64, PIPE ? 1 : 2) void attn_kernel(const AttnA
         if (t >= 1) values_from((t - 1) % 3, pf, vf);
         logits_from(t & 1, k0, sacc, scaled_tag);
         __builtin_amdgcn_s_setprio(0);
-        if (grp == 1) complete(t + 1);
+        if (!AHEAD && grp == 1) complete(t + 1);
         __syncthreads();
         // H2(t)
-        if (grp == 1) issue(t + 2);
+        if (!AHEAD && grp == 1) issue(t + 2);
         probs(sacc, pf, scaled_tag);
         read_v0(t % 3, vf);
         if (grp == 0) complete(t + 1);
+        if (AHEAD && grp == 1) {
+          complete(t + 2);
+          issue(t + 3);
+        }
         __syncthreads();
       }
       values_from((n - 1) % 3, pf, vf);

@@ -362,6 +362,36 @@ def long_history_bench(reps=10):
                 long_history_best_tflops=round(flop / res[best] / 1e9, 1))
 
 
+def head_share_bench(reps=20):
+    """One GPU's share of the layer shape when the 16 heads are spread over 8
+    GPUs: 2 heads at the full sequence lengths (7,936 queries x 25,216 keys,
+    bf16 window). The 2 x 31 query-tile blocks alone fill a quarter of the
+    chip, so the automatic plan splits the keys; both are timed."""
+    import dataclasses
+    import torch
+    from segment_autoregressive_dit_amd import nomas, synth
+
+    wl = dataclasses.replace(synth.WORKLOADS["layer_bf16"], n_heads=2)
+    H, D = wl.n_heads, wl.head_dim
+    cache = nomas.KVCache(H, D, wl.tpf, wl.capacity_frames, False)
+    kb, vb = synth.prefill_kv(wl)
+    cache.nomas_kvcache_append(dev_bf16(kb), dev_bf16(vb), wl.cached_frames)
+    q, k, v = (dev_bf16(t) for t in synth.current_qkv(wl))
+    out = torch.empty_like(q)
+    flop = wl.attention_flop()
+    res = {}
+    for splits in (1, 0):
+        ws = nomas.workspace_for(cache, wl.n_video, wl.n_text, splits)
+        res[splits] = time_calls(lambda: nomas.nomas_segment_attention(q, k, v, wl.n_video, wl.n_text, cache, out=out,
+                                                                       n_splits=splits, workspace=ws), reps)
+    auto = nomas.nomas_segment_attention_splits(wl.n_video, wl.n_text, cache.n_cached, H, D, 0, 0)
+    log(f"[bench] 2-head share: splits 1 {res[1]:.3f} ms, auto ({auto}) {res[0]:.3f} ms "
+        f"({flop / res[0] / 1e9:.1f} TFLOP/s)")
+    return dict(head_share_2_ms={"1": round(res[1], 4), "auto": round(res[0], 4)}, head_share_2_auto_splits=auto,
+                head_share_2_tflops=round(flop / res[0] / 1e9, 1),
+                head_share_2_pct_mfma_peak=round(100 * flop / res[0] / 1e9 / PEAK_BF16_TFLOPS, 2))
+
+
 def denoise_bench(n_turns=3):
     """54 layers x 8 Euler steps x n_turns against INT8 18-frame windows."""
     import torch
@@ -772,6 +802,7 @@ def main():
         extra.update(layer_int8_bench())
         extra.update(attention_cold_bench())
         extra.update(long_history_bench())
+        extra.update(head_share_bench())
     if not args.no_denoise and not args.headline_only:
         d = denoise_bench()
         extra.update(denoise_sparse_ms_per_step=round(d["denoise_sparse_ms_per_step"], 3),

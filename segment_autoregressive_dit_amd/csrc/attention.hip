@@ -1080,13 +1080,23 @@ static int key_tile(int D, bool i8) {
 // resident blocks per CU: the ping-pong schedule runs one 8-wave block per CU
 static int blocks_per_cu(int D) { return (D == 128 ? Shape<128, false>::PIPE : Shape<64, false>::PIPE) ? 1 : 2; }
 
+// Split count for a call whose query-tile blocks do not fill the chip. With s
+// splits the call runs ceil(blocks * s / slots) rounds of resident blocks, each
+// block taking 1/s of a whole block's keys; the plan takes the smallest s whose
+// makespan is within 10 % of the shortest (each split adds an fp32 partial that
+// the blocks write and the merge reads).
+// Splits keep at least 16 key tiles each, and at most 16 are used.
 static int auto_splits(int n_qtiles, int H, int tiles_total, int per_cu) {
-  const int blocks = n_qtiles * H, slots = per_cu * kCUs;
+  const int64_t blocks = (int64_t)n_qtiles * H, slots = (int64_t)per_cu * kCUs;
   if (blocks >= slots) return 1;
-  int s = (slots + blocks - 1) / blocks;
-  const int max_s = tiles_total / 16;   // at least 16 key tiles per split
-  if (s > max_s) s = max_s;
-  return s < 1 ? 1 : s;
+  const int max_s = std::min(16, tiles_total / 16);
+  if (max_s <= 1) return 1;
+  auto makespan = [&](int s) { return (double)((blocks * s + slots - 1) / slots) / s; };
+  double best = makespan(1);
+  for (int s = 2; s <= max_s; ++s) best = std::min(best, makespan(s));
+  for (int s = 1; s < max_s; ++s)
+    if (makespan(s) <= best * 1.10) return s;
+  return max_s;
 }
 
 static bool make_plan(int n_video, int n_text, int64_t n_cached, int H, int D, int kv_dtype, int n_splits,

@@ -182,6 +182,16 @@ def test_long_history_splits(splits):
     _run(synth.WORKLOADS["long_bf16"], n_splits=splits, full=True)
 
 
+@pytest.mark.parametrize("splits", [1, 0])
+@pytest.mark.parametrize("int8", [False, True])
+def test_head_share_of_eight_gpus(int8, splits):
+    # one GPU's share when the 16 heads are spread over 8 GPUs: 2 heads at the
+    # full sequence lengths (7,936 queries x 25,216 keys), every row; with
+    # n_splits = 0 the plan splits the keys to fill the chip
+    base = synth.WORKLOADS["layer_int8" if int8 else "layer_bf16"]
+    _run(synth.Workload(**{**base.__dict__, "n_heads": 2}), n_splits=splits, full=True)
+
+
 def test_split_results_agree():
     # every split count gives the same answer to within fp32 merge rounding
     wl = synth.WORKLOADS["long_bf16"]

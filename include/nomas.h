@@ -474,6 +474,21 @@ int32_t nomas_block_causal_attention(const uint16_t* q, const uint16_t* k, const
                                      float softmax_scale, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* ---- Counter calibration (a measurement aid, not a step of the method) -----
+ *
+ * For the callers that profile the library: rocprofv3's FETCH_SIZE scales
+ * differently for different access patterns, and the attention and projection
+ * kernels fetch their tiles with global -> LDS copies (16 bytes per lane). This
+ * call fetches exactly `bytes` bytes of src that way, each byte once, and
+ * writes one 32-bit word per 1 MiB slice to sink (its values mean nothing), so
+ * FETCH_SIZE of one launch over a known size gives that pattern's scale.
+ * src: (device) 16-byte aligned, bytes > 0 and a multiple of 1024; sink:
+ * (device) 4-byte aligned, nomas_calibrate_lds_stream_blocks(bytes) words.
+ * Errors: NOMAS_E_INVALID for other sizes or alignments (nothing enqueued).
+ */
+int64_t nomas_calibrate_lds_stream_blocks(int64_t bytes);   /* -1 for an invalid size */
+int32_t nomas_calibrate_lds_stream(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnomas.so")
 DEBUG_LIB = os.path.join(HERE, "libnomas_debug.so")   # the checking build (NOMAS_DEVICE_CHECKS)
 SOURCES = ["nomas_host.cpp", "rope3d.hip", "kvcache_append.hip", "kvcache_archive.cpp", "attention.hip",
-           "sparse_select.hip", "qkv_gemm.hip"]
+           "sparse_select.hip", "qkv_gemm.hip", "calibrate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -65,6 +65,8 @@ def lib():
     seg_p = ctypes.POINTER(Segment)
     sig = {
         "nomas_version": (i32, []),
+        "nomas_calibrate_lds_stream_blocks": (i64, [i64]),
+        "nomas_calibrate_lds_stream": (i32, [vp, i64, vp, vp]),
         "nomas_device_check_failures": (i64, [i32]),
         "nomas_last_error": (ctypes.c_char_p, []),
         "nomas_kvcache_token_pitch": (i64, [i32, i32]),
@@ -259,6 +261,25 @@ def nomas_rope3d(q, k, t0, n_frames, grid_h, grid_w, band, n_heads, head_dim, th
     d_t, d_h, d_w = band
     _check(lib().nomas_rope3d(qp, kp, ld, n_heads, head_dim, t0, n_frames, grid_h, grid_w,
                               d_t, d_h, d_w, float(theta), int(bool(inverse)), _stream(stream)))
+
+
+def nomas_calibrate_lds_stream(src, sink=None, stream=None):
+    """Fetch every byte of the contiguous CUDA tensor ``src`` once by global ->
+    LDS copies (the counter calibration of that access pattern); ``sink``:
+    int32 [nomas_calibrate_lds_stream_blocks(bytes)], allocated if not given."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous CUDA tensor")
+    nbytes = src.numel() * src.element_size()
+    blocks = lib().nomas_calibrate_lds_stream_blocks(nbytes)
+    if blocks < 1:
+        raise ValueError("src must hold a positive multiple of 1024 bytes")
+    if sink is None:
+        sink = _on_stream(torch.empty(blocks, dtype=torch.int32, device=src.device), stream)
+    elif sink.dtype != torch.int32 or not sink.is_cuda or not sink.is_contiguous() or sink.numel() < blocks:
+        raise ValueError(f"sink must be a contiguous int32 CUDA tensor of at least {blocks} elements")
+    _check(lib().nomas_calibrate_lds_stream(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                            _stream(stream)))
+    return sink
 
 
 def nomas_segment_attention_workspace_bytes(n_video, n_text, n_cached, n_heads, head_dim, kv_dtype, n_splits=0):

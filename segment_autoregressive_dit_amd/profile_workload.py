@@ -19,7 +19,12 @@ Summarize rocprofv3 SQLite results (``*_results.db``) into short text files::
     python -m segment_autoregressive_dit_amd.profile_workload mfma DB --kernel attn_kernel \\
         --algorithmic-flop F --out FILE.json --command "..."
 
-``traffic`` also reports the matched dispatches' average duration in the
+Counter figures are medians over the matching dispatches (a run's set-up
+launches of the same kernel, such as an append workload's pre-fill, have other
+sizes). ``calibration`` records the counters' scale for the plain copy and for
+the global -> LDS stream (``run --kernel ldscopy``).
+
+``traffic`` also reports the matched dispatches' median duration in the
 counter runs and the HBM rate it implies (counter runs serialise kernels, so the
 duration can read a little long). ``mfma`` reads a run of rocprofv3's derived
 counters ``MfmaUtil`` (MFMA busy cycles over active cycles of all SIMDs, %) and
@@ -33,6 +38,7 @@ import json
 import os
 import re
 import sqlite3
+import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +71,15 @@ def cmd_run(a):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         print(f"copy: {a.reps} x {a.bytes} bytes", file=sys.stderr)
+        return
+    if a.kernel == "ldscopy":
+        src = torch.ones(a.bytes, dtype=torch.uint8, device="cuda")
+        sink = nomas.nomas_calibrate_lds_stream(src)
+        torch.cuda.synchronize()
+        for _ in range(a.reps):
+            nomas.nomas_calibrate_lds_stream(src, sink)
+        torch.cuda.synchronize()
+        print(f"ldscopy: {a.reps + 1} x {a.bytes} bytes", file=sys.stderr)
         return
     wl = synth.WORKLOADS[a.workload]
     H, D = wl.n_heads, wl.head_dim
@@ -130,7 +145,8 @@ def cmd_trace(a):
     print(text)
 
 
-def _counter_per_dispatch(db, counter, kernel_substr):
+def _per_dispatch(db, counter, kernel_substr):
+    """{dispatch id: counter value summed over its instances} of the matching kernel."""
     con = sqlite3.connect(db)
     cur = con.cursor()
     rows = cur.execute("select kernel_name, dispatch_id, counter_name, value from counters_collection").fetchall()
@@ -141,8 +157,16 @@ def _counter_per_dispatch(db, counter, kernel_substr):
             per[did] += val
     if not per:
         raise SystemExit(f"no {counter} values for a kernel matching {kernel_substr!r} in {db}")
-    vals = list(per.values())
-    return sum(vals) / len(vals), len(vals)
+    return per
+
+
+def _counter_per_dispatch(db, counter, kernel_substr):
+    """Median over the matching dispatches and their number. The median, not the
+    mean: a run's set-up launches of the same kernel (the pre-fill append of an
+    append workload, the fill that initialises the copy's source) have other
+    sizes and would otherwise enter the figure."""
+    vals = list(_per_dispatch(db, counter, kernel_substr).values())
+    return statistics.median(vals), len(vals)
 
 
 def _dispatch_duration_ns(db, counter, kernel_substr):
@@ -151,7 +175,7 @@ def _dispatch_duration_ns(db, counter, kernel_substr):
     rows = cur.execute("select dispatch_id, kernel_name, counter_name, duration from counters_collection").fetchall()
     con.close()
     per = {did: dur for did, kn, cn, dur in rows if cn == counter and kernel_substr in kn}
-    return sum(per.values()) / len(per) if per else None
+    return statistics.median(per.values()) if per else None
 
 
 def cmd_traffic(a):
@@ -215,11 +239,31 @@ def cmd_mfma(a):
     print(json.dumps(out, indent=1))
 
 
+def cmd_calibration(a):
+    """FETCH_SIZE / WRITE_SIZE scale for the two ways the library's kernels read
+    memory: the plain copy (16-byte register loads and stores) and the
+    global -> LDS stream (buffer_load ... lds, the attention and projection
+    tiles), each over a known number of bytes."""
+    out = {"bytes": a.bytes, "command": a.command, "patterns": {}}
+    for name, db, counter, kern in (("copy_fetch", a.copy_fetch, "FETCH_SIZE", a.copy_kernel),
+                                    ("copy_write", a.copy_write, "WRITE_SIZE", a.copy_kernel),
+                                    ("lds_stream_fetch", a.lds_fetch, "FETCH_SIZE", "lds_stream")):
+        per = _per_dispatch(db, counter, kern)
+        out["patterns"][name] = {
+            "kib_per_dispatch": [round(v, 3) for v in per.values()],
+            "factor": statistics.median(per.values()) * 1024 / a.bytes,
+        }
+    with open(a.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--kernel", choices=["attention", "rope", "append", "qkv", "copy"], required=True)
+    r.add_argument("--kernel", choices=["attention", "rope", "append", "qkv", "copy", "ldscopy"], required=True)
     r.add_argument("--workload", default="layer_bf16")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--splits", type=int, default=0)
@@ -247,8 +291,14 @@ def main(argv=None):
     m.add_argument("--source", default="attention.hip")
     m.add_argument("--algorithmic-flop", type=float, default=0.0)
     m.add_argument("--command", default="")
+    c = sub.add_parser("calibration")
+    for k in ("--copy-fetch", "--copy-write", "--lds-fetch", "--out"):
+        c.add_argument(k, required=True)
+    c.add_argument("--bytes", type=int, required=True)
+    c.add_argument("--copy-kernel", default="neg")
+    c.add_argument("--command", default="")
     a = p.parse_args(argv)
-    {"run": cmd_run, "trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
+    {"run": cmd_run, "trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma, "calibration": cmd_calibration}[a.cmd](a)
 
 
 if __name__ == "__main__":

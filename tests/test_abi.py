@@ -400,3 +400,16 @@ def test_attention_frames_rejects_frames_not_retained():
                                              ctypes.c_float(0.125), 0, ws, 64, None)
     assert small == nomas.NOMAS_E_WORKSPACE
     assert d.frames_written == 6
+
+
+def test_lds_stream_calibration_sizes_and_refusals():
+    """The counter-calibration stream takes whole KiB and one sink word per MiB
+    slice, and refuses other sizes and misaligned buffers before any launch."""
+    L = nomas.lib()
+    assert [L.nomas_calibrate_lds_stream_blocks(b) for b in (0, -1024, 1000, 1024, 1 << 20, (1 << 20) + 1024)] == \
+        [-1, -1, -1, 1, 1, 2]
+    dummy = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below is refused on the host
+    assert L.nomas_calibrate_lds_stream(dummy, 1000, dummy, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_calibrate_lds_stream(None, 1024, dummy, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_calibrate_lds_stream(ctypes.c_void_p((1 << 20) + 8), 1024, dummy, None) == nomas.NOMAS_E_INVALID
+    assert L.nomas_calibrate_lds_stream(dummy, 1024, ctypes.c_void_p((1 << 20) + 2), None) == nomas.NOMAS_E_INVALID

@@ -1085,11 +1085,11 @@ static int blocks_per_cu(int D) { return (D == 128 ? Shape<128, false>::PIPE : S
 // block taking 1/s of a whole block's keys; the plan takes the smallest s whose
 // makespan is within 10 % of the shortest (each split adds an fp32 partial that
 // the blocks write and the merge reads).
-// Splits keep at least 16 key tiles each, and at most 16 are used.
+// Splits keep at least 16 key tiles each; more than one per CU never pays.
 static int auto_splits(int n_qtiles, int H, int tiles_total, int per_cu) {
   const int64_t blocks = (int64_t)n_qtiles * H, slots = (int64_t)per_cu * kCUs;
   if (blocks >= slots) return 1;
-  const int max_s = std::min(16, tiles_total / 16);
+  const int max_s = std::min(kCUs, tiles_total / 16);
   if (max_s <= 1) return 1;
   auto makespan = [&](int s) { return (double)((blocks * s + slots - 1) / slots) / s; };
   double best = makespan(1);

@@ -189,7 +189,7 @@ def test_automatic_split_count_minimises_rounds():
     """n_splits = 0 at the layer lengths (7,936 queries in 31 blocks per head,
     197 bf16 / 394 INT8 key tiles): with s splits the call runs
     ceil(31*H*s / 256) rounds of blocks that each take 1/s of the keys; the plan
-    takes the smallest s within 10 % of the shortest such makespan (s <= 16,
+    takes the smallest s within 10 % of the shortest such makespan (s <= 256,
     >= 16 key tiles per split), and 1 once the blocks fill the 256 CUs."""
     import math
     L = nomas.lib()
@@ -198,7 +198,7 @@ def test_automatic_split_count_minimises_rounds():
         blocks = 31 * H
         if blocks >= 256:
             return 1
-        span = {s: math.ceil(blocks * s / 256) / s for s in range(1, min(16, tiles // 16) + 1)}
+        span = {s: math.ceil(blocks * s / 256) / s for s in range(1, min(256, tiles // 16) + 1)}
         best = min(span.values())
         return min(s for s in span if span[s] <= best * 1.10)
 
@@ -207,6 +207,10 @@ def test_automatic_split_count_minimises_rounds():
             assert L.nomas_segment_attention_splits(7680, 256, 17280, H, 128, dt, 0) == expected(H, tiles), H
     # one GPU's share of 8-way head sharding (2 heads): 62 blocks x 4 = one round
     assert expected(2) == 4 and expected(1) == 8 and expected(16) == 1
+    # one query against a long history (721 key tiles, so at most 45 splits of
+    # 16 tiles): one block per split, and 41 is the smallest count within 10 %
+    # of the 45-split makespan
+    assert L.nomas_segment_attention_splits(0, 1, 92160, 1, 128, nomas.NOMAS_KV_BF16, 0) == 41
 
 
 def test_sparse_split_plan_can_leave_a_split_without_tiles():

@@ -192,6 +192,17 @@ def test_head_share_of_eight_gpus(int8, splits):
     _run(synth.Workload(**{**base.__dict__, "n_heads": 2}), n_splits=splits, full=True)
 
 
+@pytest.mark.parametrize("int8", [False, True])
+def test_one_query_long_history_many_splits(int8):
+    # one text query of one head against 84,480 cached keys: the automatic plan
+    # cuts the keys into 38 (bf16) or 75 (INT8) splits of one block each, and
+    # the merge combines them
+    base = synth.WORKLOADS["long_bf16"]
+    wl = synth.Workload(**{**base.__dict__, "n_heads": 1, "kv_int8": int8})
+    assert nomas.nomas_segment_attention_splits(0, 1, wl.n_cached, 1, wl.head_dim, int(int8), 0) == (75 if int8 else 38)
+    _run(wl, n_video=0, n_text=1, full=True)
+
+
 def test_split_results_agree():
     # every split count gives the same answer to within fp32 merge rounding
     wl = synth.WORKLOADS["long_bf16"]

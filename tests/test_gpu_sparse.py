@@ -92,6 +92,30 @@ def test_sparse_attention_given_lists(int8, splits, D):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("int8", [False, True])
+def test_sparse_automatic_many_splits(int8, D):
+    # one head, 3 query blocks against lists of 100 of 113 candidate blocks (the
+    # short last one included): the automatic plan cuts the listed rows several
+    # ways (one block per split), so splits that get no key tile and the merge
+    # of many partials are both exercised
+    H, tpf, nv, nt = 1, 240, 480, 40
+    (q, k, v), cache, x, kp, vp = _setup(H, D, tpf, 60, nv, nt, int8, seed=20 + int8)
+    nc = sparse.n_candidates(kp.shape[0])
+    assert nc == 113
+    lists = _random_lists(H, 3, nc, 100, seed=30 + D)
+    splits = nomas.nomas_segment_attention_splits(nv, nt, 100 * 128, H, D, int(int8), 0)
+    assert splits >= 6, splits
+    say(f"sparse attention, automatic {splits} splits: int8={int8} D={D}")
+    lse = torch.empty(H * (nv + nt), dtype=torch.float32, device="cuda")
+    out = nomas.nomas_segment_attention_sparse(q, k, v, nv, nt, cache, torch.from_numpy(lists).cuda(), lse=lse,
+                                               n_splits=0)
+    torch.cuda.synchronize()
+    ref, ref_lse = sparse.sparse_segment_attention(x[0], x[1], x[2], kp, vp, lists, 1 / math.sqrt(D))
+    _check(host_f64(out), ref, "sparse attention, automatic splits")
+    assert np.max(np.abs(lse.cpu().numpy().reshape(H, -1) - ref_lse)) <= LSE_TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("int8", [False, True])
 def test_all_blocks_equals_dense(int8, D):
     H, tpf, nv, nt = 2, 240, 480, 40
     (q, k, v), cache, _, kp, _ = _setup(H, D, tpf, 6, nv, nt, int8, seed=2)

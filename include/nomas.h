@@ -213,9 +213,10 @@ size_t nomas_segment_attention_workspace_bytes(int32_t n_video, int32_t n_text, 
 
 /* The split count the call will use for these sizes (n_splits = 0 chooses; a
  * request above the number of key tiles is clamped to it). -1 on invalid
- * arguments. The automatic choice is 1 when the call's query-tile blocks (one
- * per head and 256 queries at head dim 128) fill the 256 compute units;
- * otherwise, with s splits the call runs ceil(blocks * s / 256) rounds of
+ * arguments. The automatic choice is 1 when the call's query-tile blocks (per
+ * head, 256 queries each at head dim 128) fill the chip's resident block slots
+ * (one per compute unit at head dim 128, two at 64; 256 compute units);
+ * otherwise, with s splits the call runs ceil(blocks * s / slots) rounds of
  * blocks that each take 1/s of the keys, and it takes the smallest s within
  * 10 % of the shortest such makespan, keeping at least 16 key tiles per split. */
 int32_t nomas_segment_attention_splits(int32_t n_video, int32_t n_text, int64_t n_cached,
